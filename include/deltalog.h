@@ -1,0 +1,142 @@
+/*
+ * deltalog.h -- C ABI of libdeltalog: the DeltaLog recurrent-state decode step
+ * for linear attention (GDN, KDA, RWKV6) on AMD Instinct MI355X (gfx950).
+ *
+ * What it computes.  "DeltaLog: Deferred Materialization of Recurrent States
+ * for Linear Attention Decoding" (arXiv 2608.15533; abstract on the fugumt.com
+ * paper page, technical summary on gist.science).  Each (slot, head) keeps a
+ * d_k x d_v fp32 state ("Problem" section: S_t is d_k x d_v, held as a
+ * [B,H,d_k,d_v] tensor).  Eager decoding rewrites the whole state every token.
+ * DeltaLog keeps a dense base S-bar plus a bounded log of compact factors
+ * (a_t, b_t) and log-decay snapshots Lambda ("Core mechanism: Base + Log"):
+ * M-1 of every M steps only append to the log, the M-th merges the log into
+ * S-bar with one dense write.  Outputs equal eager decoding's up to floating
+ * point rounding (abstract: the model observes the same dense state).
+ *
+ * Operators ("Kernel implementation" section), per slot-head, with X the
+ * d_k x d_v state (row i = key i, column j = value j), ell_t the log-decay
+ * (<= 0; one per head for GDN, one per key for KDA/RWKV6), D_t = diag(e^ell_t):
+ *   GDN, KDA (delta rule):  X' = D_t X;  b_t = beta_t (v_t - X'^T k_t);
+ *                           X_t = X' + k_t b_t^T;  o_t = X_t^T q_t
+ *   RWKV6 (raw update):     o_t = X_{t-1}^T r_t + (r_t . (u (.) k_t)) v_t;
+ *                           X_t = D_t X_{t-1} + k_t v_t^T
+ * (In the common S = X^T notation of GDN/KDA: S_t = S_{t-1} D_t +
+ * beta_t (v_t - S_{t-1} D_t k_t) k_t^T, o_t = S_t q_t.)
+ *
+ * Log contents (the pages name a_t, b_t, Lambda without formulas; the reading
+ * implemented here): a_t = k_t; b_t = the delta-rule b_t above (fp32), or v_t
+ * for RWKV6 (input dtype); Lambda_t = cumulative log-decay since the last
+ * merge.  Between steps the logical state is
+ *   X = e^{Lambda_n} (.)row S-bar + sum_{j<=n} (e^{Lambda_n - Lambda_j} (.) a_j) b_j^T.
+ *
+ * Memory layouts (all row-major, all device memory, all caller-owned):
+ *   state / base   [B,H,d_k,d_v] fp32, 16-byte aligned
+ *   q (r), k       [B,H,d_k]   input dtype          v  [B,H,d_v] input dtype
+ *   beta           [B,H] fp32 (GDN, KDA; NULL for RWKV6)
+ *   log_decay      GDN [B,H] fp32; KDA, RWKV6 [B,H,d_k] fp32 (natural log, <= 0)
+ *   u              RWKV6 bonus [H,d_k] fp32 (NULL for GDN, KDA)
+ *   o              [B,H,d_v] fp32, 16-byte aligned
+ *   workspace      dl_workspace_bytes() bytes, 256-byte aligned; holds the log
+ *                  and per-step coefficients; contents need no initialisation
+ * Supported shapes: d_k, d_v in {16, 32, 64, 128}; 1 <= M <= 32; B, H >= 1
+ * with B*H*d_k*d_v < 2^31.  All B slots step in lockstep (one shared log
+ * length).
+ *
+ * Errors and ownership.  Every call returns a dl_status and never aborts or
+ * throws.  Arguments are validated on the host before any HIP call (so bad
+ * arguments are reported the same way with or without a GPU).  Kernel launch
+ * failures return DL_E_HIP.  All calls are asynchronous on `stream` (a
+ * hipStream_t; NULL = the default stream): a DL_OK return says the work was
+ * queued, not that it finished.  The library never allocates or frees device
+ * memory; the handle is host memory owned by the library (create/destroy).
+ * A handle is not thread-safe; calls on one handle must be ordered on one
+ * stream.
+ */
+#ifndef DELTALOG_H
+#define DELTALOG_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { DL_OP_GDN = 0, DL_OP_KDA = 1, DL_OP_RWKV6 = 2 } dl_op;
+typedef enum { DL_F32 = 0, DL_BF16 = 1 } dl_dtype;
+typedef enum {
+    DL_OK = 0,
+    DL_E_INVALID = 1, /* null pointer, bad enum, B/H/M out of range, missing beta or u */
+    DL_E_SHAPE = 2,   /* d_k or d_v not supported, or the state too large */
+    DL_E_ALIGN = 3,   /* a pointer is not aligned as required above */
+    DL_E_HIP = 4,     /* a HIP launch failed */
+    DL_E_STATE = 5    /* call out of order (e.g. append without replay prep) */
+} dl_status;
+
+typedef struct dl_state dl_state; /* opaque host-side handle */
+
+/* Bytes of device workspace a handle of this shape needs (0 if the arguments
+ * are invalid). */
+size_t dl_workspace_bytes(int B, int H, int d_k, int d_v, int M, dl_op op, dl_dtype in_dtype);
+
+/* Create a handle over caller-owned device memory.  `base` holds the initial
+ * state S-bar_0 [B,H,d_k,d_v] fp32 and is updated in place on merge steps;
+ * `workspace` has dl_workspace_bytes() bytes; `u` is RWKV6's bonus [H,d_k]
+ * (NULL otherwise).  The log starts empty.  *out receives the handle. */
+dl_status dl_state_create(int B, int H, int d_k, int d_v, int M, dl_op op, dl_dtype in_dtype,
+                          float *base, void *workspace, const float *u, dl_state **out);
+
+/* One decode step for all B*H slot-heads (append phase, or the merge phase on
+ * the step that brings the log to M entries).  Writes o_t [B,H,d_v] fp32.
+ * q is r for RWKV6.  beta may be NULL for RWKV6.  Equivalent to
+ * dl_replay_prep followed by dl_append_decode. */
+dl_status dl_decode_step(dl_state *s, const void *q, const void *k, const void *v,
+                         const float *beta, const float *log_decay, float *o, void *stream);
+
+/* Stage 1 of a decode step ("Kernel implementation": the shared ReplayPrep
+ * stage, once per slot-head): cumulative log-decay, replay coefficients of the
+ * n pending entries against q_t and k_t, q.k (RWKV6: r.(u (.) k)), and the
+ * key-side append (a = k, Lambda snapshot).  Must be followed by
+ * dl_append_decode with the same q and k before any other call on s. */
+dl_status dl_replay_prep(dl_state *s, const void *q, const void *k, const float *log_decay,
+                         void *stream);
+
+/* Stage 2 of a decode step (AppendDecode, parallel over value tiles): streams
+ * S-bar, adds the replayed log, writes o_t and the value-side factor b_t; on
+ * the M-th step also folds the whole log into S-bar (one dense write). */
+dl_status dl_append_decode(dl_state *s, const void *q, const void *k, const void *v,
+                           const float *beta, float *o, void *stream);
+
+/* Merge now: fold the n pending entries into S-bar so that `base` holds the
+ * logical state; empties the log.  No-op (DL_OK) when the log is empty. */
+dl_status dl_merge(dl_state *s, void *stream);
+
+/* Empty the log without folding it (S-bar is left as is): drops the pending
+ * updates.  For restarting a handle over a freshly written base. */
+dl_status dl_state_reset(dl_state *s);
+
+/* Number of pending log entries, 0..M-1 (-1 for a NULL handle). */
+int dl_log_len(const dl_state *s);
+
+/* Set the number of pending entries to n (0..M-1) after the caller restored
+ * base and workspace contents saved at that log length (exact mid-cycle
+ * checkpoint/restore). */
+dl_status dl_set_log_len(dl_state *s, int n);
+
+/* Release the handle (not the caller's device memory).  NULL is accepted. */
+dl_status dl_state_destroy(dl_state *s);
+
+/* The same-GPU baseline: one eager step that reads and rewrites the whole
+ * state S [B,H,d_k,d_v] every token (the "dense recurrent" schedule the pages
+ * compare against).  u is RWKV6's bonus [H,d_k]. */
+dl_status dl_eager_step(dl_op op, int B, int H, int d_k, int d_v, dl_dtype in_dtype, float *S,
+                        const void *q, const void *k, const void *v, const float *beta,
+                        const float *log_decay, const float *u, float *o, void *stream);
+
+/* Static description of a status code. */
+const char *dl_status_string(dl_status st);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DELTALOG_H */

@@ -1,0 +1,315 @@
+// dl_api.hip -- the C ABI of libdeltalog (include/deltalog.h): argument
+// validation, the per-handle append/merge schedule, and kernel dispatch.
+//
+// Schedule ("Core mechanism: Base + Log" in the gist.science technical summary
+// of DeltaLog): the host keeps the log length n of each handle.  A step with
+// n + 1 < M is an append step (ReplayPrep, then AppendDecode without a state
+// write); the step with n + 1 == M is the merge step (AppendDecode folds all M
+// entries into S-bar and writes it once) and leaves n = 0.  The schedule is
+// decided on the host from n alone, so no device-to-host read is ever needed.
+#include <new>
+
+#include "deltalog.h"
+#include "dl_internal.h"
+
+struct dl_state {
+    int B, H, dk, dv, M;
+    dl_op op;
+    dl_dtype dtype;
+    float *base;
+    char *ws;
+    const float *u;
+    dl::Layout lay;
+    int n;        // pending log entries
+    bool prepped; // ReplayPrep ran for the step in progress
+};
+
+namespace dl {
+
+static size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+Layout workspace_layout(long BH, int dk, int dv, int M, int op, int dtype)
+{
+    const size_t es = dtype == BF16 ? 2 : 4; // input element size
+    Layout l{};
+    l.cstride = 2 * M + 2;
+    l.a_off = 0;
+    l.b_off = round_up(l.a_off + (size_t)BH * M * dk * es, 256);
+    const size_t bsz = op == RWKV6 ? es : 4;
+    l.L_off = round_up(l.b_off + (size_t)BH * M * dv * bsz, 256);
+    const size_t lsz = op == GDN ? (size_t)BH * M * 4 : (size_t)BH * M * dk * 4;
+    l.c_off = round_up(l.L_off + lsz, 256);
+    l.total = round_up(l.c_off + (size_t)BH * l.cstride * 4, 256);
+    return l;
+}
+
+} // namespace dl
+
+namespace {
+
+bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+dl_status check_shape(int B, int H, int dk, int dv, int M, int op, int dtype)
+{
+    if (op < DL_OP_GDN || op > DL_OP_RWKV6 || (dtype != DL_F32 && dtype != DL_BF16))
+        return DL_E_INVALID;
+    if (B <= 0 || H <= 0 || M < 1 || M > 32)
+        return DL_E_INVALID;
+    if (!dim_ok(dk) || !dim_ok(dv))
+        return DL_E_SHAPE;
+    if ((long long)B * H * dk * dv >= (1LL << 31))
+        return DL_E_SHAPE;
+    return DL_OK;
+}
+
+// inputs of one step: q, k, v in the input dtype, beta/log-decay fp32, o fp32;
+// the log-decay is checked only when the call reads it (need_ld)
+dl_status check_step_ptrs(int op, int dtype, const void *q, const void *k, const void *v,
+                          const float *beta, const float *ld, const float *o, bool need_ld)
+{
+    if (!q || !k || !v || !o || (need_ld && !ld))
+        return DL_E_INVALID;
+    if (op != DL_OP_RWKV6 && !beta)
+        return DL_E_INVALID;
+    const size_t es = dtype == DL_BF16 ? 2 : 4;
+    if (!aligned(q, es) || !aligned(k, es) || !aligned(v, es) || (ld && !aligned(ld, 4)) ||
+        (beta && !aligned(beta, 4)) || !aligned(o, 16))
+        return DL_E_ALIGN;
+    return DL_OK;
+}
+
+dl::StepArgs make_args(const dl_state *s)
+{
+    dl::StepArgs a{};
+    a.BH = s->B * s->H;
+    a.H = s->H;
+    a.M = s->M;
+    a.n = s->n;
+    a.u = s->u;
+    a.base = s->base;
+    a.alog = s->ws + s->lay.a_off;
+    a.blog = s->ws + s->lay.b_off;
+    a.Llog = reinterpret_cast<float *>(s->ws + s->lay.L_off);
+    a.coef = reinterpret_cast<float *>(s->ws + s->lay.c_off);
+    a.cstride = s->lay.cstride;
+    return a;
+}
+
+hipError_t launch_prep(int op, int dtype, int dk, const dl::StepArgs &a, hipStream_t st)
+{
+    switch (op) {
+    case DL_OP_GDN: return dl::launch_prep_gdn(dtype, dk, a, st);
+    case DL_OP_KDA: return dl::launch_prep_kda(dtype, dk, a, st);
+    default: return dl::launch_prep_rwkv6(dtype, dk, a, st);
+    }
+}
+
+hipError_t launch_state(int op, int dtype, int dk, int dv, int mode, const dl::StepArgs &a,
+                        hipStream_t st)
+{
+    switch (op) {
+    case DL_OP_GDN: return dl::launch_state_gdn(dtype, dk, dv, mode, a, st);
+    case DL_OP_KDA: return dl::launch_state_kda(dtype, dk, dv, mode, a, st);
+    default: return dl::launch_state_rwkv6(dtype, dk, dv, mode, a, st);
+    }
+}
+
+} // namespace
+
+extern "C" {
+
+size_t dl_workspace_bytes(int B, int H, int d_k, int d_v, int M, dl_op op, dl_dtype in_dtype)
+{
+    if (check_shape(B, H, d_k, d_v, M, op, in_dtype) != DL_OK)
+        return 0;
+    return dl::workspace_layout((long)B * H, d_k, d_v, M, op, in_dtype).total;
+}
+
+dl_status dl_state_create(int B, int H, int d_k, int d_v, int M, dl_op op, dl_dtype in_dtype,
+                          float *base, void *workspace, const float *u, dl_state **out)
+{
+    if (!out)
+        return DL_E_INVALID;
+    *out = nullptr;
+    const dl_status st = check_shape(B, H, d_k, d_v, M, op, in_dtype);
+    if (st != DL_OK)
+        return st;
+    if (!base || !workspace || (op == DL_OP_RWKV6 && !u))
+        return DL_E_INVALID;
+    if (!aligned(base, 16) || !aligned(workspace, 256) || (u && !aligned(u, 4)))
+        return DL_E_ALIGN;
+    dl_state *s = new (std::nothrow) dl_state;
+    if (!s)
+        return DL_E_INVALID;
+    s->B = B;
+    s->H = H;
+    s->dk = d_k;
+    s->dv = d_v;
+    s->M = M;
+    s->op = op;
+    s->dtype = in_dtype;
+    s->base = base;
+    s->ws = static_cast<char *>(workspace);
+    s->u = op == DL_OP_RWKV6 ? u : nullptr;
+    s->lay = dl::workspace_layout((long)B * H, d_k, d_v, M, op, in_dtype);
+    s->n = 0;
+    s->prepped = false;
+    *out = s;
+    return DL_OK;
+}
+
+dl_status dl_replay_prep(dl_state *s, const void *q, const void *k, const float *log_decay,
+                         void *stream)
+{
+    if (!s || !q || !k || !log_decay)
+        return DL_E_INVALID;
+    if (s->prepped)
+        return DL_E_STATE;
+    const size_t es = s->dtype == DL_BF16 ? 2 : 4;
+    if (!aligned(q, es) || !aligned(k, es) || !aligned(log_decay, 4))
+        return DL_E_ALIGN;
+    dl::StepArgs a = make_args(s);
+    a.q = q;
+    a.k = k;
+    a.ld = log_decay;
+    if (launch_prep(s->op, s->dtype, s->dk, a, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return DL_E_HIP;
+    s->prepped = true;
+    return DL_OK;
+}
+
+dl_status dl_append_decode(dl_state *s, const void *q, const void *k, const void *v,
+                           const float *beta, float *o, void *stream)
+{
+    if (!s)
+        return DL_E_INVALID;
+    if (!s->prepped)
+        return DL_E_STATE;
+    // this stage does not read the log-decay: ReplayPrep stored Lam'
+    const dl_status st = check_step_ptrs(s->op, s->dtype, q, k, v, beta, nullptr, o, false);
+    if (st != DL_OK)
+        return st;
+    dl::StepArgs a = make_args(s);
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.beta = beta;
+    a.o = o;
+    const bool merge = s->n + 1 == s->M;
+    if (launch_state(s->op, s->dtype, s->dk, s->dv, merge ? dl::MERGE : dl::APPEND, a,
+                     static_cast<hipStream_t>(stream)) != hipSuccess)
+        return DL_E_HIP;
+    s->prepped = false;
+    s->n = merge ? 0 : s->n + 1;
+    return DL_OK;
+}
+
+dl_status dl_decode_step(dl_state *s, const void *q, const void *k, const void *v,
+                         const float *beta, const float *log_decay, float *o, void *stream)
+{
+    if (!s)
+        return DL_E_INVALID;
+    if (s->prepped)
+        return DL_E_STATE;
+    const dl_status st = check_step_ptrs(s->op, s->dtype, q, k, v, beta, log_decay, o, true);
+    if (st != DL_OK)
+        return st;
+    const dl_status p = dl_replay_prep(s, q, k, log_decay, stream);
+    if (p != DL_OK)
+        return p;
+    return dl_append_decode(s, q, k, v, beta, o, stream);
+}
+
+dl_status dl_merge(dl_state *s, void *stream)
+{
+    if (!s)
+        return DL_E_INVALID;
+    if (s->prepped)
+        return DL_E_STATE;
+    if (s->n == 0)
+        return DL_OK;
+    dl::StepArgs a = make_args(s);
+    if (launch_state(s->op, s->dtype, s->dk, s->dv, dl::FOLD, a, static_cast<hipStream_t>(stream)) !=
+        hipSuccess)
+        return DL_E_HIP;
+    s->n = 0;
+    return DL_OK;
+}
+
+dl_status dl_state_reset(dl_state *s)
+{
+    if (!s)
+        return DL_E_INVALID;
+    s->n = 0;
+    s->prepped = false;
+    return DL_OK;
+}
+
+int dl_log_len(const dl_state *s) { return s ? s->n : -1; }
+
+dl_status dl_set_log_len(dl_state *s, int n)
+{
+    if (!s)
+        return DL_E_INVALID;
+    if (n < 0 || n >= s->M)
+        return DL_E_INVALID;
+    if (s->prepped)
+        return DL_E_STATE;
+    s->n = n;
+    return DL_OK;
+}
+
+dl_status dl_state_destroy(dl_state *s)
+{
+    delete s;
+    return DL_OK;
+}
+
+dl_status dl_eager_step(dl_op op, int B, int H, int d_k, int d_v, dl_dtype in_dtype, float *S,
+                        const void *q, const void *k, const void *v, const float *beta,
+                        const float *log_decay, const float *u, float *o, void *stream)
+{
+    dl_status st = check_shape(B, H, d_k, d_v, 1, op, in_dtype);
+    if (st != DL_OK)
+        return st;
+    if (!S || (op == DL_OP_RWKV6 && !u))
+        return DL_E_INVALID;
+    st = check_step_ptrs(op, in_dtype, q, k, v, beta, log_decay, o, true);
+    if (st != DL_OK)
+        return st;
+    if (!aligned(S, 16) || (u && !aligned(u, 4)))
+        return DL_E_ALIGN;
+    dl::StepArgs a{};
+    a.BH = B * H;
+    a.H = H;
+    a.M = 1;
+    a.n = 0;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.beta = beta;
+    a.ld = log_decay;
+    a.u = op == DL_OP_RWKV6 ? u : nullptr;
+    a.base = S;
+    a.o = o;
+    if (launch_state(op, in_dtype, d_k, d_v, dl::EAGER, a, static_cast<hipStream_t>(stream)) !=
+        hipSuccess)
+        return DL_E_HIP;
+    return DL_OK;
+}
+
+const char *dl_status_string(dl_status st)
+{
+    switch (st) {
+    case DL_OK: return "ok";
+    case DL_E_INVALID: return "invalid argument";
+    case DL_E_SHAPE: return "unsupported shape";
+    case DL_E_ALIGN: return "misaligned pointer";
+    case DL_E_HIP: return "HIP launch failed";
+    case DL_E_STATE: return "call out of order";
+    }
+    return "unknown status";
+}
+
+} // extern "C"

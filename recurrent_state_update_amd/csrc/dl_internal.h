@@ -1,0 +1,66 @@
+// dl_internal.h -- declarations shared by the host API and the kernel files of
+// libdeltalog.  Not installed; the public interface is include/deltalog.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dl {
+
+enum Op : int { GDN = 0, KDA = 1, RWKV6 = 2 };
+enum DType : int { F32 = 0, BF16 = 1 };
+
+// What one launch of the state kernel does with a tile of the state.
+enum Mode : int {
+    APPEND = 0, // append phase: read S-bar, outputs + b_t, no state write
+    MERGE = 1,  // merge phase: as APPEND, then fold all M entries, write S-bar
+    EAGER = 2,  // eager baseline: decay, delta rule, rank-1 update, write state
+    FOLD = 3    // standalone merge: fold the n pending entries, write S-bar
+};
+
+// Byte offsets of the log and coefficient arrays inside the workspace.
+// Each segment starts on a 256-byte boundary.
+struct Layout {
+    size_t a_off;   // a-log      [B*H, M, d_k]  input dtype (a_j = k_j)
+    size_t b_off;   // b-log      [B*H, M, d_v]  fp32 (delta rule) / input dtype (RWKV6)
+    size_t L_off;   // Lambda-log [B*H, M] (GDN) or [B*H, M, d_k] fp32
+    size_t c_off;   // coef       [B*H, cstride] fp32: c^q_0..M-1, c^k_0..M-1, kappa
+    size_t total;
+    int cstride;
+};
+
+Layout workspace_layout(long BH, int dk, int dv, int M, int op, int dtype);
+
+// Everything a launch needs, passed by value as the kernel argument.
+struct StepArgs {
+    int BH;          // slot-heads
+    int H;           // heads (RWKV6's bonus u is per head)
+    int M;           // merge interval
+    int n;           // log entries before this step
+    const void *q;   // [BH, dk] (r for RWKV6)
+    const void *k;   // [BH, dk]
+    const void *v;   // [BH, dv]
+    const float *beta; // [BH]
+    const float *ld;   // [BH] (GDN) or [BH, dk]: this step's log-decay (EAGER and prep)
+    const float *u;    // [H, dk] (RWKV6)
+    float *base;       // [BH, dk, dv]
+    float *o;          // [BH, dv]
+    void *alog;
+    void *blog;
+    float *Llog;
+    float *coef;
+    int cstride;
+};
+
+// Kernel launchers, one set per operator (dl_gdn.hip, dl_kda.hip, dl_rwkv6.hip).
+// They return the launch status (hipGetLastError after the launch) or
+// hipErrorInvalidValue for an unsupported shape.
+hipError_t launch_prep_gdn(int dtype, int dk, const StepArgs &a, hipStream_t st);
+hipError_t launch_prep_kda(int dtype, int dk, const StepArgs &a, hipStream_t st);
+hipError_t launch_prep_rwkv6(int dtype, int dk, const StepArgs &a, hipStream_t st);
+hipError_t launch_state_gdn(int dtype, int dk, int dv, int mode, const StepArgs &a, hipStream_t st);
+hipError_t launch_state_kda(int dtype, int dk, int dv, int mode, const StepArgs &a, hipStream_t st);
+hipError_t launch_state_rwkv6(int dtype, int dk, int dv, int mode, const StepArgs &a, hipStream_t st);
+
+} // namespace dl

@@ -1,0 +1,16 @@
+// dl_kda.hip -- instantiates the ReplayPrep and state kernels for KDA.
+#include "dl_kernels.h"
+
+namespace dl {
+
+hipError_t launch_prep_kda(int dtype, int dk, const StepArgs &a, hipStream_t st)
+{
+    return launch_prep<KDA>(dtype, dk, a, st);
+}
+
+hipError_t launch_state_kda(int dtype, int dk, int dv, int mode, const StepArgs &a, hipStream_t st)
+{
+    return launch_state<KDA>(dtype, dk, dv, mode, a, st);
+}
+
+} // namespace dl

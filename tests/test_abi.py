@@ -1,0 +1,135 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/deltalog.h declares, and rejects bad arguments with the
+documented status codes before any HIP call.  No call here reaches a kernel
+launch: every handle is built over fake (never dereferenced) addresses and
+only invalid calls, or calls that return before launching, are made."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import recurrent_state_update_amd as rsu
+from recurrent_state_update_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "deltalog.h")
+
+OK, INVALID, SHAPE, ALIGN, HIP, STATE = range(6)
+GDN, KDA, RWKV6 = 0, 1, 2
+F32, BF16 = 0, 1
+# fake device addresses: aligned, never dereferenced by these tests
+BASE, WS, U, Q, K, V, BETA, LD, O = (0x7f0000000000 + 0x100000 * i for i in range(9))
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dl_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported():
+    names = declared_functions()
+    assert len(names) >= 12
+    out = subprocess.run(["nm", "-D", "--defined-only", rsu.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (dl_\w+)$", out, flags=re.M))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    for n in names:
+        assert hasattr(_lib, n)
+    assert set(rsu.EXPORTS) == set(names)
+
+
+def test_status_strings():
+    for st in range(6):
+        assert rsu.dl_status_string(st)
+    assert rsu.dl_status_string(99) == "unknown status"
+
+
+def test_workspace_bytes():
+    assert rsu.dl_workspace_bytes(64, 32, 128, 128, 8, GDN, BF16) > 0
+    ws_gdn = rsu.dl_workspace_bytes(64, 32, 128, 128, 8, GDN, BF16)
+    ws_kda = rsu.dl_workspace_bytes(64, 32, 128, 128, 8, KDA, BF16)
+    assert ws_kda > ws_gdn  # per-key Lambda snapshots
+    # a-log bf16 + b-log fp32 + Lambda + coefficients, each 256-B aligned
+    BH, M = 64 * 32, 8
+    expect = BH * M * 128 * 2 + BH * M * 128 * 4 + BH * M * 4 + BH * (2 * M + 2) * 4
+    assert expect <= ws_gdn < expect + 4 * 256
+    for bad in [(0, 1, 16, 16, 4, GDN, F32), (1, 0, 16, 16, 4, GDN, F32), (1, 1, 16, 16, 0, GDN, F32),
+                (1, 1, 16, 16, 33, GDN, F32), (1, 1, 24, 16, 4, GDN, F32), (1, 1, 16, 256, 4, GDN, F32),
+                (1, 1, 16, 16, 4, 3, F32), (1, 1, 16, 16, 4, GDN, 2)]:
+        assert rsu.dl_workspace_bytes(*bad) == 0, bad
+
+
+def _create(B=2, H=3, dk=16, dv=16, M=4, op=GDN, dt=F32, base=BASE, ws=WS, u=None):
+    return rsu.dl_state_create(B, H, dk, dv, M, op, dt, base, ws, u)
+
+
+def test_create_validation():
+    assert _create(dk=24)[0] == SHAPE
+    assert _create(dv=256)[0] == SHAPE
+    assert _create(M=0)[0] == INVALID and _create(M=33)[0] == INVALID
+    assert _create(B=0)[0] == INVALID and _create(H=-1)[0] == INVALID
+    assert _create(op=5)[0] == INVALID and _create(dt=7)[0] == INVALID
+    assert _create(base=None)[0] == INVALID and _create(ws=None)[0] == INVALID
+    assert _create(op=RWKV6, u=None)[0] == INVALID
+    assert _create(base=BASE + 4)[0] == ALIGN
+    assert _create(ws=WS + 16)[0] == ALIGN
+    assert _create(B=1 << 16, H=1 << 8, dk=128, dv=128)[0] == SHAPE  # state >= 2^31 elements
+    st = _lib.dl_state_create(1, 1, 16, 16, 4, GDN, F32, BASE, WS, None, None)
+    assert st == INVALID  # NULL out-pointer
+    st, h = _create()
+    assert st == OK and h
+    assert rsu.dl_log_len(h) == 0
+    assert rsu.dl_state_destroy(h) == OK
+    st, h = _create(op=RWKV6, u=U)
+    assert st == OK
+    rsu.dl_state_destroy(h)
+
+
+def test_step_validation_before_any_launch():
+    st, h = _create(op=GDN, dt=BF16)
+    assert st == OK
+    try:
+        s = 0  # stream: never used, every call below fails validation
+        assert rsu.dl_decode_step(h, None, K, V, BETA, LD, O, s) == INVALID
+        assert rsu.dl_decode_step(h, Q, K, V, None, LD, O, s) == INVALID      # beta for GDN
+        assert rsu.dl_decode_step(h, Q, K, V, BETA, None, O, s) == INVALID
+        assert rsu.dl_decode_step(h, Q, K, V, BETA, LD, None, s) == INVALID
+        assert rsu.dl_decode_step(h, Q + 1, K, V, BETA, LD, O, s) == ALIGN   # bf16 needs 2 B
+        assert rsu.dl_decode_step(h, Q, K, V, BETA, LD, O + 4, s) == ALIGN   # o needs 16 B
+        assert rsu.dl_decode_step(h, Q, K, V, BETA + 2, LD, O, s) == ALIGN
+        assert rsu.dl_append_decode(h, Q, K, V, BETA, O, s) == STATE          # no prep yet
+        assert rsu.dl_replay_prep(h, None, K, LD, s) == INVALID
+        assert rsu.dl_replay_prep(h, Q, K, LD + 1, s) == ALIGN
+        assert rsu.dl_merge(h, s) == OK                                       # empty log: no-op
+        assert rsu.dl_log_len(h) == 0
+        assert rsu.dl_set_log_len(h, 4) == INVALID and rsu.dl_set_log_len(h, -1) == INVALID
+        assert rsu.dl_set_log_len(h, 3) == OK and rsu.dl_log_len(h) == 3
+        assert rsu.dl_state_reset(h) == OK and rsu.dl_log_len(h) == 0
+        assert rsu.dl_merge(None, s) == INVALID
+        assert rsu.dl_log_len(None) == -1
+    finally:
+        rsu.dl_state_destroy(h)
+    assert rsu.dl_state_destroy(None) == OK
+
+
+def test_eager_validation_before_any_launch():
+    s = 0
+    e = rsu.dl_eager_step
+    assert e(GDN, 1, 1, 16, 16, F32, None, Q, K, V, BETA, LD, None, O, s) == INVALID
+    assert e(GDN, 1, 1, 24, 16, F32, BASE, Q, K, V, BETA, LD, None, O, s) == SHAPE
+    assert e(GDN, 1, 1, 16, 16, F32, BASE, Q, K, V, None, LD, None, O, s) == INVALID
+    assert e(RWKV6, 1, 1, 16, 16, F32, BASE, Q, K, V, None, LD, None, O, s) == INVALID  # u missing
+    assert e(GDN, 1, 1, 16, 16, F32, BASE + 8, Q, K, V, BETA, LD, None, O, s) == ALIGN
+    assert e(GDN, 1, 1, 16, 16, F32, BASE, Q + 2, K, V, BETA, LD, None, O, s) == ALIGN  # f32 needs 4 B
+    assert e(KDA, 0, 1, 16, 16, F32, BASE, Q, K, V, BETA, LD, None, O, s) == INVALID
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        rsu.DeltaLogState("gdn", 1, 2, 16, 16, 4, dtype=torch.float32,
+                          base=torch.zeros(1, 2, 16, 16))

@@ -1,0 +1,194 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 eager oracle,
+element by element, on seeded synthetic workloads.
+
+Checked every step: o_t.  Checked after every merge (and after forced merges):
+the dense base S-bar, which must equal the eager state.  Bar: max-abs relative
+error below the pages' 5e-3, and below the tighter fp32 bound FP32_TOL."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_harness import FP32_TOL, PAGES_TOL, ParityRun, dev, in_dtype, rel, sample_slot_heads
+
+pytestmark = pytest.mark.gpu
+
+needs_gpu = pytest.mark.skipif(not torch.cuda.is_available(), reason="no GPU")
+
+
+def _report(run, name):
+    print(f"[{name}] steps={run.t} worst o={run.worst_o:.2e} worst S={run.worst_S:.2e} "
+          f"(states checked {run.checked_S})", flush=True)
+    assert run.worst_o < PAGES_TOL and run.worst_S < PAGES_TOL
+    assert run.worst_o < FP32_TOL and run.worst_S < FP32_TOL
+
+
+@needs_gpu
+def test_tiny_gdn_workload_full(orc):
+    """GDN B=1 H=2 d=16 M=4, 32 steps, fp32: every output and every merge."""
+    w = synth.WORKLOADS[0]
+    run = ParityRun(w, orc=orc)
+    for _ in range(w.steps):
+        run.step()
+    assert run.checked_S == w.steps // w.M
+    _report(run, "w0")
+    run.close()
+
+
+@needs_gpu
+@pytest.mark.parametrize("wid", [1, 2, 3])
+def test_serving_ops_reduced_batch(orc, wid):
+    """Workloads 1-3 at their d and M, with B*H cut to 15 slot-heads (ragged
+    over the 8 XCDs and over 4-wave ReplayPrep groups), 3 merge cycles."""
+    w = synth.WORKLOADS[wid].with_(B=3, H=5)
+    run = ParityRun(w, orc=orc)
+    for _ in range(3 * w.M):
+        run.step()
+    _report(run, f"w{wid} B=3 H=5")
+    run.close()
+
+
+@needs_gpu
+@pytest.mark.parametrize("op", ["gdn", "kda", "rwkv6"])
+@pytest.mark.parametrize("dk", [16, 32, 64, 128])
+@pytest.mark.parametrize("dv", [16, 32, 64, 128])
+def test_all_shapes(orc, op, dk, dv):
+    """Every supported (d_k, d_v) for every op, bf16 inputs, M=3, 7 steps
+    (two merges and a pending log), then a forced merge."""
+    w = synth.Workload(9, op, 2, 3, dk, dv, 3, 7, "bf16")
+    run = ParityRun(w, orc=orc)
+    for _ in range(7):
+        run.step()
+    run.merge()
+    _report(run, f"{op} dk={dk} dv={dv}")
+    run.close()
+
+
+@needs_gpu
+@pytest.mark.parametrize("op", ["gdn", "kda", "rwkv6"])
+@pytest.mark.parametrize("M", [1, 2, 4, 5, 8, 16, 32])
+def test_merge_intervals(orc, op, M):
+    """Outputs every step and the base after every merge, for M from 1
+    (eager) to the maximum 32."""
+    w = synth.Workload(10, op, 2, 4, 64, 64, M, max(2 * M, 8), "bf16")
+    run = ParityRun(w, orc=orc)
+    for _ in range(w.steps):
+        run.step()
+    run.merge()
+    _report(run, f"{op} M={M}")
+    run.close()
+
+
+@needs_gpu
+@pytest.mark.parametrize("op", ["gdn", "kda", "rwkv6"])
+def test_forced_merge_at_every_log_length(orc, op):
+    """dl_merge after n = 1..M-1 appends gives the eager state; a second
+    merge is a no-op; the schedule then continues correctly."""
+    M = 8
+    for stop in range(1, M):
+        w = synth.Workload(11, op, 1, 5, 128, 128, M, stop, "bf16")
+        run = ParityRun(w, orc=orc)
+        for _ in range(stop):
+            run.step()
+        assert run.st.log_len == stop
+        run.merge()
+        before = run.state_gpu().copy()
+        run.merge()
+        assert np.array_equal(before, run.state_gpu())
+        for _ in range(M + 1):
+            run.step()
+        _report(run, f"{op} forced merge at n={stop}")
+        run.close()
+
+
+@needs_gpu
+@pytest.mark.parametrize("wid", [0, 1, 2, 3])
+def test_eager_kernel(orc, wid):
+    """The eager baseline kernel against the oracle (reduced batch)."""
+    w = synth.WORKLOADS[wid]
+    if wid:
+        w = w.with_(B=2, H=7)
+    run = ParityRun(w, eager=True, orc=orc)
+    for _ in range(12):
+        run.step()
+    _report(run, f"eager w{wid}")
+
+
+@needs_gpu
+@pytest.mark.parametrize("op", ["gdn", "kda", "rwkv6"])
+def test_m1_matches_eager_kernel(op):
+    """M = 1 DeltaLog and the eager kernel compute the same recurrence."""
+    w = synth.Workload(12, op, 2, 3, 128, 64, 1, 6, "bf16")
+    a = ParityRun(w)
+    b = ParityRun(w, eager=True)
+    for t in range(6):
+        s = synth.step(w, t)
+        a.step(s)
+        b.step(s)
+        assert rel(a.state_gpu(), b.state_gpu()) < 1e-5
+    a.close()
+
+
+@needs_gpu
+def test_staged_calls_equal_decode_step():
+    """dl_replay_prep + dl_append_decode is bit-identical to dl_decode_step,
+    and two runs are bit-identical (no atomics, fixed reduction order)."""
+    w = synth.Workload(13, "kda", 2, 3, 128, 128, 4, 10, "bf16")
+    runs = [ParityRun(w) for _ in range(3)]
+    for t in range(10):
+        s = synth.step(w, t)
+        runs[0].step(s)
+        runs[1].step(s, staged=True)
+        runs[2].step(s)
+    g = [r.state_gpu() for r in runs]
+    assert np.array_equal(g[0], g[1]) and np.array_equal(g[0], g[2])
+    for r in runs:
+        r.close()
+
+
+@needs_gpu
+def test_call_order_errors():
+    import recurrent_state_update_amd as rsu
+    w = synth.Workload(14, "gdn", 1, 2, 16, 16, 4, 2, "f32")
+    run = ParityRun(w)
+    s = synth.step(w, 0)
+    q, k, ld = dev(s["q"]), dev(s["k"]), dev(s["ld"])
+    run.st.replay_prep(q, k, ld)
+    with pytest.raises(rsu.DeltaLogError):
+        run.st.replay_prep(q, k, ld)          # prep twice
+    with pytest.raises(rsu.DeltaLogError):
+        run.st.merge()                        # merge between the stages
+    run.st.append_decode(q, k, dev(s["v"]), dev(s["beta"]))
+    assert run.st.log_len == 1
+    run.close()
+
+
+@needs_gpu
+@pytest.mark.parametrize("op", ["gdn", "rwkv6"])
+def test_checkpoint_restore_mid_cycle(op):
+    """Saving base + workspace at log length n and restoring them into a new
+    handle continues bit-identically to the uninterrupted run."""
+    import recurrent_state_update_amd as rsu
+    w = synth.Workload(15, op, 2, 2, 64, 64, 8, 14, "bf16")
+    X0, u = synth.initial(w)
+    dt = in_dtype(w)
+    a = rsu.DeltaLogState(op, w.B, w.H, w.dk, w.dv, w.M, dtype=dt, base=dev(X0), u=dev(u))
+    inputs = [synth.step(w, t) for t in range(w.steps)]
+
+    def go(st, s):
+        return st.step(dev(s["q"], dt), dev(s["k"], dt), dev(s["v"], dt), dev(s["beta"]), dev(s["ld"]))
+
+    for t in range(3):
+        go(a, inputs[t])
+    snap_base, snap_ws, n = a.base.clone(), a.workspace.clone(), a.log_len
+    assert n == 3
+    outs_a = [go(a, inputs[t]).cpu() for t in range(3, w.steps)]
+    b = rsu.DeltaLogState(op, w.B, w.H, w.dk, w.dv, w.M, dtype=dt, base=snap_base, u=dev(u))
+    b.workspace.copy_(snap_ws)
+    b.set_log_len(n)
+    outs_b = [go(b, inputs[t]).cpu() for t in range(3, w.steps)]
+    for x, y in zip(outs_a, outs_b):
+        assert torch.equal(x, y)
+    a.merge()
+    b.merge()
+    assert torch.equal(a.base, b.base)
