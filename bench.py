@@ -111,35 +111,44 @@ def make_states(w, R: int, dt):
 
 
 # ------------------------------------------------------------------- timing --
+def _ptrs(inp, s):
+    """Raw device addresses of step s's inputs (so the timed loop does no
+    tensor indexing)."""
+    g = lambda key: None if inp[key] is None else inp[key][s].data_ptr()
+    return g("q"), g("k"), g("v"), g("beta"), g("ld")
+
+
 def run_deltalog(w, inp, sts, K: int, W: int, instrument: bool):
     """W warm-up + K timed steps, state i % R at step i.  Returns wall ms,
-    per-launch state-kernel ms (list of (ms, n, mode)) and prep ms."""
+    per-launch state-kernel ms (list of (ms, n, mode)) and ReplayPrep ms."""
     import torch
+    import recurrent_state_update_amd as rsu
     stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
     pool = inp["q"].shape[0]
     R = len(sts)
+    ptrs = [_ptrs(inp, s) for s in range(pool)]
+    outs = [torch.empty(w.B, w.H, w.dv, device="cuda") for _ in range(2)]
+    optr = [o.data_ptr() for o in outs]
+    hs = [st._h for st in sts]
+    prep_f, app_f = rsu._lib.dl_replay_prep, rsu._lib.dl_append_decode
 
     def one(i, evs=None):
-        st = sts[i % R]
-        s = i % pool
-        q, k, v = inp["q"][s], inp["k"][s], inp["v"][s]
-        beta = None if inp["beta"] is None else inp["beta"][s]
-        ld = inp["ld"][s]
-        n = st.log_len
+        h = hs[i % R]
+        q, k, v, beta, ld = ptrs[i % pool]
         if evs is not None:
             evs[0].record(stream)
-        st.replay_prep(q, k, ld)
+        if prep_f(h, q, k, ld, sp) != 0:
+            raise RuntimeError("dl_replay_prep failed")
         if evs is not None:
             evs[1].record(stream)
-        st.append_decode(q, k, v, beta, o=outs[i % 2])
+        if app_f(h, q, k, v, beta, optr[i % 2], sp) != 0:
+            raise RuntimeError("dl_append_decode failed")
         if evs is not None:
             evs[2].record(stream)
-        return n
 
-    outs = [torch.empty(w.B, w.H, w.dv, device="cuda") for _ in range(2)]
     for i in range(W):
         one(i)
-    torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)] if instrument else None
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
@@ -147,7 +156,8 @@ def run_deltalog(w, inp, sts, K: int, W: int, instrument: bool):
     torch.cuda.synchronize()
     t0.record(stream)
     for i in range(K):
-        ns.append(one(W + i, evs[i] if instrument else None))
+        ns.append(sts[(W + i) % R].log_len)
+        one(W + i, evs[i] if instrument else None)
     t1.record(stream)
     torch.cuda.synchronize()
     wall = t0.elapsed_time(t1)
@@ -165,17 +175,23 @@ def run_eager(w, inp, bases, u_dev, K: int, W: int, instrument: bool):
     import torch
     import recurrent_state_update_amd as rsu
     stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
     pool = inp["q"].shape[0]
     R = len(bases)
     o = torch.empty(w.B, w.H, w.dv, device="cuda")
+    ptrs = [_ptrs(inp, s) for s in range(pool)]
+    bptr = [b.data_ptr() for b in bases]
+    uptr = None if u_dev is None else u_dev.data_ptr()
+    opi, dti = rsu.OPS[w.op], rsu.DTYPES[inp["q"].dtype]
+    f = rsu._lib.dl_eager_step
 
     def one(i, evs=None):
-        s = i % pool
-        beta = None if inp["beta"] is None else inp["beta"][s]
+        q, k, v, beta, ld = ptrs[i % pool]
         if evs is not None:
             evs[0].record(stream)
-        rsu.eager_step(w.op, bases[i % R], inp["q"][s], inp["k"][s], inp["v"][s], beta,
-                       inp["ld"][s], u_dev, o=o)
+        if f(opi, w.B, w.H, w.dk, w.dv, dti, bptr[i % R], q, k, v, beta, ld, uptr,
+             o.data_ptr(), sp) != 0:
+            raise RuntimeError("dl_eager_step failed")
         if evs is not None:
             evs[1].record(stream)
 

@@ -87,8 +87,10 @@ dl_status dl_state_create(int B, int H, int d_k, int d_v, int M, dl_op op, dl_dt
 
 /* One decode step for all B*H slot-heads (append phase, or the merge phase on
  * the step that brings the log to M entries).  Writes o_t [B,H,d_v] fp32.
- * q is r for RWKV6.  beta may be NULL for RWKV6.  Equivalent to
- * dl_replay_prep followed by dl_append_decode. */
+ * q is r for RWKV6.  beta may be NULL for RWKV6.  One kernel launch: each
+ * value-tile workgroup also does its slot-head's ReplayPrep work.  Computes
+ * the same step as dl_replay_prep followed by dl_append_decode (the results
+ * agree up to floating-point summation order). */
 dl_status dl_decode_step(dl_state *s, const void *q, const void *k, const void *v,
                          const float *beta, const float *log_decay, float *o, void *stream);
 

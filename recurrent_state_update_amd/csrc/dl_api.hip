@@ -7,6 +7,11 @@
 // write); the step with n + 1 == M is the merge step (AppendDecode folds all M
 // entries into S-bar and writes it once) and leaves n = 0.  The schedule is
 // decided on the host from n alone, so no device-to-host read is ever needed.
+//
+// dl_decode_step runs the step as one launch of the fused kernel (the
+// ReplayPrep work done inside each AppendDecode workgroup); dl_replay_prep +
+// dl_append_decode run it as the two-stage split, ReplayPrep once per
+// slot-head then AppendDecode per value tile.  Both compute the same step.
 #include <new>
 
 #include "deltalog.h"
@@ -105,13 +110,13 @@ hipError_t launch_prep(int op, int dtype, int dk, const dl::StepArgs &a, hipStre
     }
 }
 
-hipError_t launch_state(int op, int dtype, int dk, int dv, int mode, const dl::StepArgs &a,
-                        hipStream_t st)
+hipError_t launch_step(int op, int dtype, int dk, int dv, int mode, const dl::StepArgs &a,
+                       hipStream_t st)
 {
     switch (op) {
-    case DL_OP_GDN: return dl::launch_state_gdn(dtype, dk, dv, mode, a, st);
-    case DL_OP_KDA: return dl::launch_state_kda(dtype, dk, dv, mode, a, st);
-    default: return dl::launch_state_rwkv6(dtype, dk, dv, mode, a, st);
+    case DL_OP_GDN: return dl::launch_step_gdn(dtype, dk, dv, mode, a, st);
+    case DL_OP_KDA: return dl::launch_step_kda(dtype, dk, dv, mode, a, st);
+    default: return dl::launch_step_rwkv6(dtype, dk, dv, mode, a, st);
     }
 }
 
@@ -197,7 +202,7 @@ dl_status dl_append_decode(dl_state *s, const void *q, const void *k, const void
     a.beta = beta;
     a.o = o;
     const bool merge = s->n + 1 == s->M;
-    if (launch_state(s->op, s->dtype, s->dk, s->dv, merge ? dl::MERGE : dl::APPEND, a,
+    if (launch_step(s->op, s->dtype, s->dk, s->dv, merge ? dl::MERGE : dl::APPEND, a,
                      static_cast<hipStream_t>(stream)) != hipSuccess)
         return DL_E_HIP;
     s->prepped = false;
@@ -215,10 +220,20 @@ dl_status dl_decode_step(dl_state *s, const void *q, const void *k, const void *
     const dl_status st = check_step_ptrs(s->op, s->dtype, q, k, v, beta, log_decay, o, true);
     if (st != DL_OK)
         return st;
-    const dl_status p = dl_replay_prep(s, q, k, log_decay, stream);
-    if (p != DL_OK)
-        return p;
-    return dl_append_decode(s, q, k, v, beta, o, stream);
+    dl::StepArgs a = make_args(s);
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.beta = beta;
+    a.ld = log_decay;
+    a.o = o;
+    const bool merge = s->n + 1 == s->M;
+    if (launch_step(s->op, s->dtype, s->dk, s->dv, merge ? dl::FMERGE : dl::FAPPEND, a,
+                    static_cast<hipStream_t>(stream)) !=
+        hipSuccess)
+        return DL_E_HIP;
+    s->n = merge ? 0 : s->n + 1;
+    return DL_OK;
 }
 
 dl_status dl_merge(dl_state *s, void *stream)
@@ -230,7 +245,7 @@ dl_status dl_merge(dl_state *s, void *stream)
     if (s->n == 0)
         return DL_OK;
     dl::StepArgs a = make_args(s);
-    if (launch_state(s->op, s->dtype, s->dk, s->dv, dl::FOLD, a, static_cast<hipStream_t>(stream)) !=
+    if (launch_step(s->op, s->dtype, s->dk, s->dv, dl::FOLD, a, static_cast<hipStream_t>(stream)) !=
         hipSuccess)
         return DL_E_HIP;
     s->n = 0;
@@ -293,7 +308,7 @@ dl_status dl_eager_step(dl_op op, int B, int H, int d_k, int d_v, dl_dtype in_dt
     a.u = op == DL_OP_RWKV6 ? u : nullptr;
     a.base = S;
     a.o = o;
-    if (launch_state(op, in_dtype, d_k, d_v, dl::EAGER, a, static_cast<hipStream_t>(stream)) !=
+    if (launch_step(op, in_dtype, d_k, d_v, dl::EAGER, a, static_cast<hipStream_t>(stream)) !=
         hipSuccess)
         return DL_E_HIP;
     return DL_OK;

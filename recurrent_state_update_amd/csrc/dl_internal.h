@@ -11,12 +11,14 @@ namespace dl {
 enum Op : int { GDN = 0, KDA = 1, RWKV6 = 2 };
 enum DType : int { F32 = 0, BF16 = 1 };
 
-// What one launch of the state kernel does with a tile of the state.
+// What one launch of the step kernel does with a tile of the state.
 enum Mode : int {
-    APPEND = 0, // append phase: read S-bar, outputs + b_t, no state write
-    MERGE = 1,  // merge phase: as APPEND, then fold all M entries, write S-bar
-    EAGER = 2,  // eager baseline: decay, delta rule, rank-1 update, write state
-    FOLD = 3    // standalone merge: fold the n pending entries, write S-bar
+    APPEND = 0,  // two-stage append phase: read S-bar, outputs + b_t, no state write
+    MERGE = 1,   // two-stage merge phase: as APPEND, then fold all M entries, write S-bar
+    EAGER = 2,   // eager baseline: decay, delta rule, rank-1 update, write state
+    FOLD = 3,    // standalone merge: fold the n pending entries, write S-bar
+    FAPPEND = 4, // one-launch append phase (replay coefficients computed in place)
+    FMERGE = 5   // one-launch merge phase
 };
 
 // Byte offsets of the log and coefficient arrays inside the workspace.
@@ -59,8 +61,8 @@ struct StepArgs {
 hipError_t launch_prep_gdn(int dtype, int dk, const StepArgs &a, hipStream_t st);
 hipError_t launch_prep_kda(int dtype, int dk, const StepArgs &a, hipStream_t st);
 hipError_t launch_prep_rwkv6(int dtype, int dk, const StepArgs &a, hipStream_t st);
-hipError_t launch_state_gdn(int dtype, int dk, int dv, int mode, const StepArgs &a, hipStream_t st);
-hipError_t launch_state_kda(int dtype, int dk, int dv, int mode, const StepArgs &a, hipStream_t st);
-hipError_t launch_state_rwkv6(int dtype, int dk, int dv, int mode, const StepArgs &a, hipStream_t st);
+hipError_t launch_step_gdn(int dtype, int dk, int dv, int mode, const StepArgs &a, hipStream_t st);
+hipError_t launch_step_kda(int dtype, int dk, int dv, int mode, const StepArgs &a, hipStream_t st);
+hipError_t launch_step_rwkv6(int dtype, int dk, int dv, int mode, const StepArgs &a, hipStream_t st);
 
 } // namespace dl

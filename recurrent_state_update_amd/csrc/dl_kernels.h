@@ -29,11 +29,14 @@
 // HBM-bound and uses no MFMA.  Each workgroup owns one (slot-head, value tile
 // of T columns).  A lane owns 4 adjacent columns (one 128-bit load per row) and
 // P rows; a row of T columns is read by T/4 adjacent lanes, so a wave's load
-// covers whole contiguous row segments.  All P row loads are issued before any
-// use.  Column sums over rows reduce across lanes with xor-shuffles and across
-// waves through LDS; the small per-step metadata (value-side log shard,
-// coefficients, fold table) is staged in LDS while the base loads are in
-// flight.  Workgroups of one slot-head are placed on the same XCD.
+// covers whole contiguous row segments.  All loads of a workgroup are issued
+// before any is used: the small ones (row metadata, the tile's log shard,
+// coefficients) first, then the P base rows, so the workgroup waits on memory
+// once.  Loads that a lane does not need are pointed past the end of a
+// bounds-limited buffer resource: they return zero without touching memory,
+// which keeps the code branch-free (no load gets sunk behind a wait) and adds
+// no traffic.  Column sums reduce across lanes with xor-shuffles and across
+// waves through LDS.  Workgroups of one slot-head are placed on the same XCD.
 #pragma once
 
 #include "dl_internal.h"
@@ -41,21 +44,16 @@
 #ifndef DL_TILE_MAX
 #define DL_TILE_MAX 64 // widest value tile (columns) per workgroup
 #endif
+#ifndef DL_MAX_M
+#define DL_MAX_M 32 // largest merge interval
+#endif
 #ifndef DL_THREADS_MAX
-#define DL_THREADS_MAX 256 // threads per workgroup of the state kernel
+#define DL_THREADS_MAX 256 // threads per workgroup of the step kernel
 #endif
 
 namespace dl {
 
 // ------------------------------------------------------------------ helpers --
-
-template <typename TIn> __device__ __forceinline__ float load_in(const TIn *p, long i);
-template <> __device__ __forceinline__ float load_in<float>(const float *p, long i) { return p[i]; }
-// bf16 held as its 16 raw bits: the fp32 with the same upper half
-template <> __device__ __forceinline__ float load_in<uint16_t>(const uint16_t *p, long i)
-{
-    return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
-}
 
 // Sum over the lanes of a wave64 whose lane ids differ only in bits >= log2(FROM).
 template <int FROM> __device__ __forceinline__ float wave_sum_from(float x)
@@ -78,6 +76,64 @@ __device__ __forceinline__ int xcd_remap(int b, int G)
     return (b % NX) * per + b / NX;
 }
 
+// Raw buffer resources: a base, a size in bytes, and loads at a 32-bit byte
+// offset (per lane) plus a wave-uniform offset.  An access at or past the size
+// reads zero and touches no memory; stores there are dropped.
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+using u32x2 = unsigned int __attribute__((ext_vector_type(2)));
+using u32x4 = unsigned int __attribute__((ext_vector_type(4)));
+constexpr int kBufferDword3 = 0x00020000;   // raw buffer, 32-bit data format (CDNA)
+constexpr unsigned kSkip = 0x80000000u;     // a byte offset past every resource here
+constexpr unsigned kSkipElem = 0x20000000u; // an element index past every resource here
+                                            // (x4 bytes still fits 32 bits)
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, unsigned bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kBufferDword3);
+}
+__device__ __forceinline__ float4 buf_ld4(rsrc_t r, unsigned off, unsigned soff = 0)
+{
+    return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0));
+}
+__device__ __forceinline__ void buf_st4(rsrc_t r, unsigned off, unsigned soff, float4 v)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, soff, 0);
+}
+__device__ __forceinline__ float buf_ldf(rsrc_t r, unsigned off)
+{
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+// One input element (fp32, or bf16 as its 16 raw bits) at element index e.
+template <typename TIn> __device__ __forceinline__ float buf_ld_in(rsrc_t r, unsigned e);
+template <> __device__ __forceinline__ float buf_ld_in<float>(rsrc_t r, unsigned e)
+{
+    return buf_ldf(r, e * 4u);
+}
+template <> __device__ __forceinline__ float buf_ld_in<uint16_t>(rsrc_t r, unsigned e)
+{
+    const unsigned short h = __builtin_amdgcn_raw_buffer_load_b16(r, e * 2u, 0, 0);
+    return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+// Four consecutive input elements at element index e (a multiple of 4).
+template <typename TIn> __device__ __forceinline__ float4 buf_ld4_in(rsrc_t r, unsigned e);
+template <> __device__ __forceinline__ float4 buf_ld4_in<float>(rsrc_t r, unsigned e)
+{
+    return buf_ld4(r, e * 4u);
+}
+template <> __device__ __forceinline__ float4 buf_ld4_in<uint16_t>(rsrc_t r, unsigned e)
+{
+    const u32x2 h = __builtin_amdgcn_raw_buffer_load_b64(r, e * 2u, 0, 0);
+    return make_float4(__uint_as_float(h[0] << 16), __uint_as_float(h[0] & 0xffff0000u),
+                       __uint_as_float(h[1] << 16), __uint_as_float(h[1] & 0xffff0000u));
+}
+// An input-dtype value back from a float that holds one exactly.
+template <typename TIn> __device__ __forceinline__ TIn to_in(float x);
+template <> __device__ __forceinline__ float to_in<float>(float x) { return x; }
+template <> __device__ __forceinline__ uint16_t to_in<uint16_t>(float x)
+{
+    return static_cast<uint16_t>(__float_as_uint(x) >> 16);
+}
+
 template <int DK, int DV> struct TileCfg {
     static constexpr int T = DV < DL_TILE_MAX ? DV : DL_TILE_MAX;            // tile columns
     static constexpr int NT = DK * T / 4 < DL_THREADS_MAX ? DK * T / 4 : DL_THREADS_MAX; // threads
@@ -85,10 +141,15 @@ template <int DK, int DV> struct TileCfg {
     static constexpr int RPP = NT / LPR;  // rows per pass of the workgroup
     static constexpr int P = DK / RPP;    // rows per lane
     static constexpr int NTILE = DV / T;
-    static constexpr int NW = (NT + 63) / 64;
-    static_assert(P * RPP == DK && LPR <= 32 && NT % LPR == 0, "tile shape");
+    static constexpr int NW = NT / 64;
+    static_assert(P * RPP == DK && LPR <= 32 && NT % LPR == 0 && NT % 64 == 0, "tile shape");
 };
 
+__host__ __device__ constexpr bool mode_fused(int mode) { return mode == FAPPEND || mode == FMERGE; }
+__host__ __device__ constexpr bool mode_logged(int mode)
+{
+    return mode == APPEND || mode == MERGE || mode_fused(mode);
+}
 // Rows of the staged value-side factors and of the fold table for a launch.
 __host__ __device__ constexpr int bt_rows(int mode, int n)
 {
@@ -96,13 +157,17 @@ __host__ __device__ constexpr int bt_rows(int mode, int n)
 }
 __host__ __device__ constexpr int fold_rows(int mode, int n)
 {
-    return mode == MERGE ? n + 1 : mode == EAGER ? 1 : mode == FOLD ? n : 0;
+    return (mode == MERGE || mode == FMERGE) ? n + 1 : mode == EAGER ? 1 : mode == FOLD ? n : 0;
 }
-// Dynamic LDS floats: Bt [bt_rows][T], F [fold_rows][DK], coefficients [2n+1].
+constexpr int kRowTables = 8;
+// Dynamic LDS floats of the step kernel: eight per-row tables [DK], Bt
+// [bt_rows][T], F [fold_rows][DK], coefficients [2n+1], then a 16-byte aligned
+// junk slot: lanes with nothing to publish store there, which keeps the
+// publishing stores unconditional.
 __host__ __device__ constexpr int dyn_floats(int mode, int n, int DK, int T)
 {
-    return bt_rows(mode, n) * T + fold_rows(mode, n) * DK +
-           ((mode == APPEND || mode == MERGE) ? 2 * n + 1 : 0);
+    return kRowTables * DK + bt_rows(mode, n) * T + fold_rows(mode, n) * DK +
+           (mode_logged(mode) ? 2 * n + 1 : 0) + 3 + 4;
 }
 
 // ------------------------------------------------------------- ReplayPrep --
@@ -116,63 +181,85 @@ template <int OP, typename TIn, int DK>
 __global__ __launch_bounds__(256) void replay_prep_kernel(StepArgs a)
 {
     constexpr int KPL = (DK + 63) / 64; // keys per lane
+    constexpr int EB = 8;               // log entries whose loads are issued together
     const int lane = threadIdx.x & 63;
     const int sh = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (sh >= a.BH)
         return; // whole wave leaves together
     const int n = a.n, M = a.M;
-    const TIn *q = static_cast<const TIn *>(a.q) + (long)sh * DK;
-    const TIn *k = static_cast<const TIn *>(a.k) + (long)sh * DK;
-    const TIn *alog = static_cast<const TIn *>(a.alog) + (long)sh * M * DK;
     float *L = a.Llog + (OP == GDN ? (long)sh * M : (long)sh * M * DK);
+    // the n logged entries of this slot-head (loads past them read zero)
+    const rsrc_t ar = make_rsrc(static_cast<const TIn *>(a.alog) + (long)sh * M * DK, n * DK * sizeof(TIn));
+    const rsrc_t lr = make_rsrc(L, (OP == GDN ? n : n * DK) * 4);
 
+    float am[EB][KPL], lm[EB][KPL], gm[EB];
+    auto load_batch = [&](int m0) {
+#pragma unroll
+        for (int e = 0; e < EB; ++e) {
+            const int m = m0 + e;
+            gm[e] = OP == GDN ? buf_ldf(lr, m < n ? (unsigned)m * 4u : kSkip) : 0.f;
+#pragma unroll
+            for (int c = 0; c < KPL; ++c) {
+                const int i = lane + 64 * c;
+                const unsigned ei = (m < n && i < DK) ? (unsigned)(m * DK + i) : kSkipElem;
+                am[e][c] = buf_ld_in<TIn>(ar, ei);
+                lm[e][c] = OP != GDN ? buf_ld_in<float>(lr, ei) : 0.f;
+            }
+        }
+    };
+    load_batch(0); // first batch of entry loads, ahead of everything else
+    const rsrc_t qr = make_rsrc(static_cast<const TIn *>(a.q) + (long)sh * DK, DK * sizeof(TIn));
+    const rsrc_t kr = make_rsrc(static_cast<const TIn *>(a.k) + (long)sh * DK, DK * sizeof(TIn));
     float qv[KPL], kv[KPL], lp[KPL], lw[KPL];
 #pragma unroll
     for (int c = 0; c < KPL; ++c) {
         const int i = lane + 64 * c;
-        const bool ok = i < DK;
-        qv[c] = ok ? load_in(q, i) : 0.f;
-        kv[c] = ok ? load_in(k, i) : 0.f;
-        if (OP == GDN) {
-            lp[c] = n > 0 ? L[n - 1] : 0.f;
-            lw[c] = lp[c] + a.ld[sh];
-        } else {
-            lp[c] = (ok && n > 0) ? L[(long)(n - 1) * DK + i] : 0.f;
-            lw[c] = lp[c] + (ok ? a.ld[(long)sh * DK + i] : 0.f);
-        }
+        const unsigned ei = i < DK ? (unsigned)i : kSkipElem;
+        qv[c] = buf_ld_in<TIn>(qr, ei);
+        kv[c] = buf_ld_in<TIn>(kr, ei);
+        // Lam_{n-1} is entry n-1 of the log (0 when the log is empty)
+        lp[c] = OP == GDN ? (n > 0 ? buf_ldf(lr, (unsigned)(n - 1) * 4u) : 0.f)
+                          : buf_ld_in<float>(lr, (n > 0 && i < DK) ? (unsigned)((n - 1) * DK + i) : kSkipElem);
+        lw[c] = lp[c] + (OP == GDN ? a.ld[sh] : (i < DK ? a.ld[(long)sh * DK + i] : 0.f));
     }
 
     float *coef = a.coef + (long)sh * a.cstride;
-    for (int m = 0; m < n; ++m) {
-        float sq = 0.f, sk = 0.f;
+    for (int m0 = 0; m0 < n; m0 += EB) {
+        if (m0 > 0)
+            load_batch(m0);
 #pragma unroll
-        for (int c = 0; c < KPL; ++c) {
-            const int i = lane + 64 * c;
-            if (i < DK) {
-                const float am = load_in(alog, (long)m * DK + i);
-                float e;
+        for (int e = 0; e < EB; ++e) {
+            const int m = m0 + e;
+            if (m >= n)
+                break; // uniform over the wave
+            float sq = 0.f, sk = 0.f;
+#pragma unroll
+            for (int c = 0; c < KPL; ++c) {
+                if (lane + 64 * c >= DK)
+                    continue;
+                float f;
                 if (OP == GDN)
-                    e = am; // scalar decay factor applied after the sum
+                    f = am[e][c]; // scalar decay factor applied after the sum
                 else if (OP == KDA)
-                    e = expf(lw[c] - L[(long)m * DK + i]) * am;
+                    f = expf(lw[c] - lm[e][c]) * am[e][c];
                 else
-                    e = expf(lp[c] - L[(long)m * DK + i]) * am;
-                sq += e * qv[c];
-                sk += e * kv[c];
+                    f = expf(lp[c] - lm[e][c]) * am[e][c];
+                sq = fmaf(f, qv[c], sq);
+                sk = fmaf(f, kv[c], sk);
             }
-        }
-        sq = wave_sum_from<1>(sq);
-        if (OP != RWKV6)
-            sk = wave_sum_from<1>(sk);
-        if (OP == GDN) {
-            const float s = expf(lw[0] - L[m]);
-            sq *= s;
-            sk *= s;
-        }
-        if (lane == 0) {
-            coef[m] = sq;
+            sq = wave_sum_from<1>(sq);
             if (OP != RWKV6)
-                coef[M + m] = sk;
+                sk = wave_sum_from<1>(sk);
+            if (OP == GDN) {
+                const float g = expf(lw[0] - gm[e]);
+                sq *= g;
+                sk *= g;
+            }
+            if (lane == 0) {
+                coef[m] = sq;
+                if (OP != RWKV6)
+                    coef[M + m] = sk;
+            }
         }
     }
 
@@ -193,7 +280,7 @@ __global__ __launch_bounds__(256) void replay_prep_kernel(StepArgs a)
     for (int c = 0; c < KPL; ++c) {
         const int i = lane + 64 * c;
         if (i < DK) {
-            an[i] = k[i];
+            an[i] = to_in<TIn>(kv[c]);
             if (OP != GDN)
                 L[(long)n * DK + i] = lw[c];
         }
@@ -202,24 +289,39 @@ __global__ __launch_bounds__(256) void replay_prep_kernel(StepArgs a)
         L[n] = lw[0];
 }
 
-// ------------------------------------------------------------ state kernel --
+// -------------------------------------------------------------- step kernel --
 //
-// AppendDecode (APPEND, MERGE), the eager baseline (EAGER) and the standalone
-// merge (FOLD) share this body; MODE selects which parts run.
-//   reads   (APPEND, MERGE, EAGER): y = X-bar^T w over the tile, outputs o_t
-//           and the value-side factor b_t of this step;
-//   writes  (MERGE, EAGER, FOLD):   fold entries into the tile, one store.
+// One body for every launch on the state, MODE selecting the parts:
+//   APPEND, MERGE    AppendDecode of the two-stage path: replay coefficients
+//                    and the key-side append come from ReplayPrep;
+//   FAPPEND, FMERGE  the one-launch path: each workgroup also computes its
+//                    slot-head's replay coefficients (wave w takes log entries
+//                    w, w+NW, ...) and tile 0 performs the key-side append;
+//   EAGER            the eager baseline: decay, delta rule or raw update,
+//                    rank-1 fold of this step only;
+//   FOLD             standalone merge of the n pending entries.
+// MERGE/FMERGE/EAGER/FOLD end with the fold and the single dense write.
 template <int OP, typename TIn, int DK, int DV, int MODE>
-__global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void state_kernel(StepArgs a)
+__global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
 {
     using C = TileCfg<DK, DV>;
     constexpr int T = C::T, NT = C::NT, LPR = C::LPR, RPP = C::RPP, P = C::P;
     constexpr int NTILE = C::NTILE, NW = C::NW;
     constexpr bool DELTA = OP != RWKV6;
-    constexpr bool READS = MODE != FOLD;
-    constexpr bool WRITES = MODE != APPEND;
-    constexpr bool LOGGED = MODE == APPEND || MODE == MERGE; // uses ReplayPrep's output
-    constexpr int NV = 9; // reduced values per column group: 4 yq, 4 yk, kappa
+    constexpr bool FUSED = mode_fused(MODE);
+    constexpr bool STAGED = MODE == APPEND || MODE == MERGE;
+    constexpr bool LOGGED = FUSED || STAGED;               // a step of the DeltaLog schedule
+    constexpr bool READS = MODE != FOLD;                   // computes o_t and b_t
+    constexpr bool MERGING = MODE == MERGE || MODE == FMERGE;
+    constexpr bool WRITES = MERGING || MODE == EAGER || MODE == FOLD;
+    constexpr bool KAPPA_HERE = FUSED || MODE == EAGER;    // q.k summed in this kernel
+    constexpr int ES = sizeof(TIn);
+    constexpr int BS = DELTA ? 4 : ES;                     // b-log element size
+    constexpr int NV = 9;                                  // 4 yq, 4 yk, kappa
+    constexpr int RW = (DK + NT - 1) / NT;                 // row-table rows per lane
+    constexpr int SB = ((DL_MAX_M - 1) * (T / 4) + NT - 1) / NT; // log-shard float4 per lane
+    constexpr int KPL = (DK + 63) / 64;                    // keys per lane, coefficient pass
+    constexpr int EW = (8 + NW - 1) / NW;                  // entries per wave, coefficient pass
 
     extern __shared__ float4 dyn4[];
     float *dyn = reinterpret_cast<float *>(dyn4);
@@ -232,93 +334,228 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void state_kernel(StepArgs a
     const int col = tile * T + 4 * c4;
     const int M = a.M, n = a.n;
 
-    // 1. issue the whole tile's loads: P rows x 128 bits per lane
     float *S = a.base + (long)sh * DK * DV;
+    float *L = a.Llog + (OP == GDN ? (long)sh * M : (long)sh * M * DK);
+
+    const int nb = bt_rows(MODE, n), nf = fold_rows(MODE, n);
+    float *Wq = dyn;             // read weights, q side
+    float *Wk = dyn + DK;        // read weights, k side
+    float *Rf = dyn + 2 * DK;    // fold base factor e^{Lam_f}
+    float *Lf = dyn + 3 * DK;    // fold log-decay Lam_f
+    float *Qk = dyn + 4 * DK;    // q.k (RWKV6: r.(u (.) k)) terms
+    float *Qr = dyn + 5 * DK;    // raw q (FUSED coefficient pass)
+    float *Kr = dyn + 6 * DK;    // raw k (FUSED)
+    float *Lx = dyn + 7 * DK;    // replay log-decay: Lam' (delta) / Lam_{n-1} (RWKV6) (FUSED)
+    float *Bt = dyn + kRowTables * DK;         // [nb][T] value-side factors of this tile
+    float *F = Bt + nb * T;                    // [nf][DK] key-side fold coefficients
+    float *cf = F + nf * DK;                   // [2n+1] c^q, c^k, kappa (LOGGED)
+    float *junk = dyn + ((kRowTables * DK + nb * T + nf * DK + (LOGGED ? 2 * n + 1 : 0) + 3) & ~3);
+
+    // ------------------------------------------------------ 0. small loads --
+    // Row metadata for rows i = tid + j*NT (lanes past d_k skip).
+    const rsrc_t q_r = make_rsrc(static_cast<const TIn *>(a.q) + (long)sh * DK, READS ? DK * ES : 0);
+    const rsrc_t k_r = make_rsrc(static_cast<const TIn *>(a.k) + (long)sh * DK, READS ? DK * ES : 0);
+    // the Lambda log: Lam_{n-1} is entry n-1, Lam_n (from ReplayPrep) entry n
+    const rsrc_t L_r = make_rsrc(L, MODE == EAGER ? 0 : (OP == GDN ? M : M * DK) * 4);
+    const rsrc_t ld_r = make_rsrc(a.ld + (OP == GDN ? sh : (long)sh * DK),
+                                  (MODE == EAGER || FUSED) ? (OP == GDN ? 1 : DK) * 4 : 0);
+    const rsrc_t u_r = make_rsrc(a.u + (long)(sh % a.H) * DK, (OP == RWKV6 && KAPPA_HERE) ? DK * 4 : 0);
+    float mq[RW], mk[RW], mprev[RW], mcur[RW], mell[RW], mu[RW];
+#pragma unroll
+    for (int j = 0; j < RW; ++j) {
+        const int i = tid + j * NT;
+        const unsigned ei = i < DK ? (unsigned)i : kSkipElem;
+        mq[j] = buf_ld_in<TIn>(q_r, ei);
+        mk[j] = buf_ld_in<TIn>(k_r, ei);
+        // per-key log-decays: Lam_{n-1} (0 when the log is empty), Lam_n, ell_t
+        mprev[j] = mcur[j] = mell[j] = 0.f;
+        if (OP != GDN) {
+            mprev[j] = buf_ld_in<float>(L_r, (n > 0 && i < DK) ? (unsigned)((n - 1) * DK + i) : kSkipElem);
+            if (STAGED)
+                mcur[j] = buf_ld_in<float>(L_r, i < DK ? (unsigned)(n * DK + i) : kSkipElem);
+            mell[j] = buf_ld_in<float>(ld_r, ei);
+        }
+        mu[j] = buf_ld_in<float>(u_r, ei);
+    }
+    // GDN: the head's scalar log-decays (wave-uniform)
+    float gprev = 0.f, gnew = 0.f;
+    if (OP == GDN) {
+        gprev = (MODE != EAGER && n > 0) ? L[n - 1] : 0.f;
+        gnew = MODE == EAGER ? a.ld[sh] : STAGED ? L[n] : MODE == FOLD ? gprev : gprev + a.ld[sh];
+    }
+    // This tile's shard of the n logged value-side factors.
+    const rsrc_t b_r = make_rsrc(static_cast<const char *>(a.blog) + (long)sh * M * DV * BS,
+                                 MODE == EAGER ? 0 : n * DV * BS);
+    float4 bst[SB];
+#pragma unroll
+    for (int s = 0; s < SB; ++s) {
+        const int idx = tid + s * NT;
+        const int m = idx / (T / 4), j4 = idx % (T / 4);
+        const unsigned e = (MODE != EAGER && idx < n * (T / 4)) ? (unsigned)(m * DV + tile * T + 4 * j4) : kSkipElem;
+        if (DELTA)
+            bst[s] = buf_ld4_in<float>(b_r, e);
+        else
+            bst[s] = buf_ld4_in<TIn>(b_r, e);
+    }
+    // ReplayPrep's coefficients (two-stage path)
+    float cst = 0.f;
+    if (STAGED) {
+        const rsrc_t c_r = make_rsrc(a.coef + (long)sh * a.cstride, a.cstride * 4);
+        const int ci = tid < n ? tid : tid < 2 * n ? M + tid - n : 2 * M;
+        cst = buf_ldf(c_r, tid < 2 * n + 1 ? (unsigned)ci * 4u : kSkip);
+    }
+    // log entries for this wave's share of the replay coefficients (FUSED)
+    float ea[EW][KPL], el[EW][KPL], eg[EW];
+    const rsrc_t a_r = make_rsrc(static_cast<const TIn *>(a.alog) + (long)sh * M * DK, FUSED ? n * DK * ES : 0);
+#pragma unroll
+    for (int e = 0; e < EW; ++e) {
+        const int m = wave + NW * e;
+        eg[e] = (FUSED && OP == GDN && m < n) ? L[m] : 0.f;
+#pragma unroll
+        for (int c = 0; c < KPL; ++c) {
+            const int i = lane + 64 * c;
+            const unsigned ei = (FUSED && m < n && i < DK) ? (unsigned)(m * DK + i) : kSkipElem;
+            ea[e][c] = buf_ld_in<TIn>(a_r, ei);
+            el[e][c] = OP != GDN ? buf_ld_in<float>(L_r, ei) : 0.f;
+        }
+    }
+    // v and beta for the lanes that finalise (lanes < LPR)
+    const rsrc_t v_r = make_rsrc(static_cast<const TIn *>(a.v) + (long)sh * DV, READS ? DV * ES : 0);
+    const float4 vv = buf_ld4_in<TIn>(v_r, (READS && tid < LPR) ? (unsigned)col : kSkipElem);
+    const float bet = (READS && DELTA) ? a.beta[sh] : 0.f;
+
+    // ------------------------------------------------ 1. the tile's base rows --
+    const rsrc_t tile_r = make_rsrc(S, DK * DV * 4);
+    const unsigned xoff = (unsigned)(r0 * DV + col) * 4u; // this lane's byte offset in a pass
     float4 x[P];
 #pragma unroll
     for (int p = 0; p < P; ++p)
-        x[p] = *reinterpret_cast<const float4 *>(S + (long)(r0 + p * RPP) * DV + col);
+        x[p] = buf_ld4(tile_r, xoff, p * RPP * DV * 4);
 
-    const TIn *q = static_cast<const TIn *>(a.q) + (long)sh * DK;
-    const TIn *k = static_cast<const TIn *>(a.k) + (long)sh * DK;
-    const float *L = a.Llog + (OP == GDN ? (long)sh * M : (long)sh * M * DK);
-
-    const int nb = bt_rows(MODE, n), nf = fold_rows(MODE, n);
-    float *Bt = dyn;                                  // [nb][T] value-side factors, this tile
-    float *F = Bt + nb * T;                           // [nf][DK] key-side fold coefficients
-    float *cf = F + (WRITES ? nf * DK : 0);           // [2n+1] c^q, c^k, kappa
-
-    // 2. stage the value-side log shard of this tile (entries < n) in LDS
-    const int nlog = (MODE == EAGER) ? 0 : n;
-    for (int idx = tid; idx < nlog * (T / 4); idx += NT) {
-        const int m = idx / (T / 4), j4 = idx % (T / 4);
-        const long off = ((long)sh * M + m) * DV + tile * T + 4 * j4;
-        float4 b;
-        if (DELTA) {
-            b = *reinterpret_cast<const float4 *>(static_cast<const float *>(a.blog) + off);
+    // ---------------------------------------- 2. publish the small data in LDS --
+#pragma unroll
+    for (int j = 0; j < RW; ++j) {
+        const int i = tid + j * NT;
+        const bool ok = i < DK;
+        // Lam' (the decayed state's cumulative log-decay) and Lam_f (fold)
+        float lnew, lfold;
+        if (OP == GDN) {
+            lnew = lfold = gnew;
         } else {
-            const TIn *bl = static_cast<const TIn *>(a.blog);
-            b = make_float4(load_in(bl, off), load_in(bl, off + 1), load_in(bl, off + 2),
-                            load_in(bl, off + 3));
+            lnew = MODE == EAGER ? mell[j] : STAGED ? mcur[j] : mprev[j] + mell[j];
+            lfold = MODE == FOLD ? mprev[j] : lnew;
         }
-        *reinterpret_cast<float4 *>(Bt + m * T + 4 * j4) = b;
-    }
-    if (LOGGED) {
-        const float *coef = a.coef + (long)sh * a.cstride;
-        for (int idx = tid; idx < 2 * n + 1; idx += NT)
-            cf[idx] = idx < n ? coef[idx] : idx < 2 * n ? coef[M + idx - n] : coef[2 * M];
-    }
-    // 3. fold table: F[m][i] = e^{Lam_f,i - Lam_m,i} a_m,i for logged entries,
-    //    k_i for this step's entry (MERGE, EAGER)
-    if (WRITES) {
-        const TIn *alog = static_cast<const TIn *>(a.alog) + (long)sh * M * DK;
-        const int lf = MODE == FOLD ? n - 1 : n;
-        for (int idx = tid; idx < nf * DK; idx += NT) {
-            const int m = idx / DK, i = idx % DK;
-            float f;
-            if (MODE == EAGER || (MODE == MERGE && m == n)) {
-                f = load_in(k, i);
-            } else {
-                const float lfv = OP == GDN ? L[lf] : L[(long)lf * DK + i];
-                const float lm = OP == GDN ? L[m] : L[(long)m * DK + i];
-                f = expf(lfv - lm) * load_in(alog, (long)m * DK + i);
-            }
-            F[idx] = f;
+        float wq, wk = 0.f;
+        if (OP == GDN) {
+            wq = mq[j];
+            wk = mk[j];
+        } else if (OP == KDA) {
+            const float e = expf(lnew);
+            wq = e * mq[j];
+            wk = e * mk[j];
+        } else {
+            wq = (MODE == EAGER ? 1.f : expf(mprev[j])) * mq[j];
         }
-    }
-    // prefetch what the finalising lanes need
-    float4 vv = make_float4(0.f, 0.f, 0.f, 0.f);
-    float bet = 0.f;
-    if (READS && tid < LPR) {
-        const TIn *v = static_cast<const TIn *>(a.v) + (long)sh * DV + col;
-        vv = make_float4(load_in(v, 0), load_in(v, 1), load_in(v, 2), load_in(v, 3));
+        (ok ? Wq + i : junk)[0] = wq;
         if (DELTA)
-            bet = a.beta[sh];
+            (ok ? Wk + i : junk)[0] = wk;
+        if (OP != GDN && WRITES) {
+            (ok ? Rf + i : junk)[0] = expf(lfold);
+            (ok ? Lf + i : junk)[0] = lfold;
+        }
+        if (KAPPA_HERE)
+            (ok ? Qk + i : junk)[0] = DELTA ? mq[j] * mk[j] : mq[j] * mu[j] * mk[j];
+        if (FUSED) {
+            (ok ? Qr + i : junk)[0] = mq[j];
+            (ok ? Kr + i : junk)[0] = mk[j];
+            (ok ? Lx + i : junk)[0] = OP == RWKV6 ? mprev[j] : lnew;
+            if (MODE == FMERGE)
+                (ok ? F + n * DK + i : junk)[0] = mk[j]; // this step's entry folds with k
+            if (MODE == FAPPEND && tile == 0 && ok) {   // key-side append of entry n
+                static_cast<TIn *>(a.alog)[((long)sh * M + n) * DK + i] = to_in<TIn>(mk[j]);
+                if (OP != GDN)
+                    L[(long)n * DK + i] = lnew;
+            }
+        }
+        if (MODE == EAGER)
+            (ok ? F + i : junk)[0] = mk[j]; // the only entry folds with k
+    }
+    if (OP == GDN && MODE == FAPPEND && tile == 0 && tid == 0)
+        L[n] = gnew;
+    if (MODE != EAGER) {
+#pragma unroll
+        for (int s = 0; s < SB; ++s) {
+            const int idx = tid + s * NT;
+            const int m = idx / (T / 4), j4 = idx % (T / 4);
+            float *dst = idx < n * (T / 4) ? Bt + m * T + 4 * j4 : junk;
+            *reinterpret_cast<float4 *>(dst) = bst[s];
+        }
+    }
+    if (STAGED)
+        (tid < 2 * n + 1 ? cf + tid : junk)[0] = cst;
+    __syncthreads();
+
+    // ------------- 3. FUSED: this wave's replay coefficients (and fold rows)
+    if (FUSED) {
+        for (int m0 = 0; m0 < n; m0 += NW * EW) {
+            if (m0 > 0) { // a log longer than one pass: load this pass's entries
+#pragma unroll
+                for (int e = 0; e < EW; ++e) {
+                    const int m = m0 + wave + NW * e;
+                    eg[e] = (OP == GDN && m < n) ? L[m] : 0.f;
+#pragma unroll
+                    for (int c = 0; c < KPL; ++c) {
+                        const int i = lane + 64 * c;
+                        const unsigned ei = (m < n && i < DK) ? (unsigned)(m * DK + i) : kSkipElem;
+                        ea[e][c] = buf_ld_in<TIn>(a_r, ei);
+                        el[e][c] = OP != GDN ? buf_ld_in<float>(L_r, ei) : 0.f;
+                    }
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < EW; ++e) {
+                const int m = m0 + wave + NW * e;
+                if (m >= n)
+                    break; // uniform over the wave
+                // GDN: the entry's scalar factor e^{Lam' - Lam_m}
+                const float g = OP == GDN ? expf(gnew - eg[e]) : 1.f;
+                float sq = 0.f, sk = 0.f;
+#pragma unroll
+                for (int c = 0; c < KPL; ++c) {
+                    const int i = lane + 64 * c;
+                    if (i >= DK)
+                        continue;
+                    // e^{Lam_x,i - Lam_m,i} a_m,i (GDN: scalar factor applied after the sum)
+                    const float f = OP == GDN ? ea[e][c] : expf(Lx[i] - el[e][c]) * ea[e][c];
+                    sq = fmaf(f, Qr[i], sq);
+                    if (DELTA)
+                        sk = fmaf(f, Kr[i], sk);
+                    if (MODE == FMERGE) // fold row: e^{Lam' - Lam_m} a_m
+                        F[m * DK + i] = OP == GDN ? g * ea[e][c]
+                                      : OP == KDA ? f
+                                                  : expf(Lf[i] - el[e][c]) * ea[e][c];
+                }
+                sq = wave_sum_from<1>(sq);
+                if (DELTA)
+                    sk = wave_sum_from<1>(sk);
+                if (lane == 0) {
+                    cf[m] = g * sq;
+                    cf[n + m] = g * sk;
+                }
+            }
+        }
     }
 
-    // 4. column sums y_q = X-bar^T w_q, y_k = X-bar^T w_k over this lane's rows
-    float rowf[P]; // per-row base factor for the fold (KDA, RWKV6)
+    // -------- 4. column sums over this lane's rows, reduced across lanes/waves
     if (READS) {
         float yq[4] = {0.f, 0.f, 0.f, 0.f}, yk[4] = {0.f, 0.f, 0.f, 0.f}, kap = 0.f;
 #pragma unroll
         for (int p = 0; p < P; ++p) {
             const int r = r0 + p * RPP;
-            const float qr = load_in(q, r), kr = load_in(k, r);
-            float wq = qr, wk = kr;
-            if (OP == KDA) {
-                const float lnew = MODE == EAGER ? a.ld[(long)sh * DK + r] : L[(long)n * DK + r];
-                const float e = expf(lnew);
-                wq *= e;
-                wk *= e;
-                rowf[p] = e;
-            } else if (OP == RWKV6) {
-                const float lprev = (MODE == EAGER || n == 0) ? 0.f : L[(long)(n - 1) * DK + r];
-                wq *= expf(lprev);
-                if (WRITES)
-                    rowf[p] = expf(MODE == EAGER ? a.ld[(long)sh * DK + r] : L[(long)n * DK + r]);
-            }
-            if (MODE == EAGER && c4 == 0)
-                kap += DELTA ? qr * kr : qr * a.u[(long)(sh % a.H) * DK + r] * kr;
+            const float wq = Wq[r];
+            const float wk = DELTA ? Wk[r] : 0.f;
+            if (KAPPA_HERE && c4 == 0)
+                kap += Qk[r];
             const float xs[4] = {x[p].x, x[p].y, x[p].z, x[p].w};
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
@@ -330,10 +567,8 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void state_kernel(StepArgs a
         float vals[NV] = {yq[0], yq[1], yq[2], yq[3], yk[0], yk[1], yk[2], yk[3], kap};
 #pragma unroll
         for (int c = 0; c < NV; ++c) {
-            if (!DELTA && c >= 4 && c < 8)
-                continue;
-            if (MODE != EAGER && c == 8)
-                continue;
+            if ((!DELTA && c >= 4 && c < 8) || (!KAPPA_HERE && c == 8))
+                continue; // identically zero
             vals[c] = wave_sum_from<LPR>(vals[c]);
         }
         if (lane < LPR) {
@@ -341,89 +576,104 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void state_kernel(StepArgs a
             for (int c = 0; c < NV; ++c)
                 red[wave][lane][c] = vals[c];
         }
-    } else if (OP != GDN) {
-        // FOLD: per-row base factor e^{Lam_{n-1}}
-#pragma unroll
-        for (int p = 0; p < P; ++p)
-            rowf[p] = expf(L[(long)(n - 1) * DK + r0 + p * RPP]);
     }
-    __syncthreads();
+    if (READS || FUSED)
+        __syncthreads();
 
-    // 5. finalise this tile's outputs (one lane per 4 columns)
-    if (READS) {
-        if (tid < LPR) {
-            float y[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            float kap = 0.f;
+    // ------- 5. fold table for MERGE / FOLD (FMERGE, EAGER built theirs above):
+    //    F[m][i] = e^{Lam_f,i - Lam_m,i} a_m,i; in MERGE the entry n appended by
+    //    ReplayPrep (a_n = k, Lam_n = Lam_f) gives exactly k_i.
+    if (MODE == MERGE || MODE == FOLD) {
+        const rsrc_t af_r = make_rsrc(static_cast<const TIn *>(a.alog) + (long)sh * M * DK, nf * DK * ES);
+        const int total = nf * DK;
+        for (int base = 0; base < total; base += 4 * NT) {
+            float av[4], lv[4];
 #pragma unroll
-            for (int w = 0; w < NW; ++w) {
-#pragma unroll
-                for (int c = 0; c < 8; ++c)
-                    y[c] += red[w][tid][c];
-                kap += red[w][0][8];
+            for (int u = 0; u < 4; ++u) {
+                const int idx = base + u * NT + tid;
+                const unsigned ei = idx < total ? (unsigned)idx : kSkipElem;
+                av[u] = buf_ld_in<TIn>(af_r, ei);
+                lv[u] = buf_ld_in<float>(L_r, OP == GDN ? (idx < total ? (unsigned)(idx / DK) : kSkipElem) : ei);
             }
-            if (OP == GDN) {
-                const float s = expf(MODE == EAGER ? a.ld[sh] : L[n]);
 #pragma unroll
-                for (int c = 0; c < 8; ++c)
-                    y[c] *= s;
+            for (int u = 0; u < 4; ++u) {
+                const int idx = base + u * NT + tid;
+                if (idx < total)
+                    F[idx] = expf((OP == GDN ? gnew : Lf[idx % DK]) - lv[u]) * av[u];
             }
-            float rq[4] = {0.f, 0.f, 0.f, 0.f}, rk[4] = {0.f, 0.f, 0.f, 0.f};
-            if (LOGGED) {
+        }
+    }
+
+    // ------------------------ 6. finalise this tile's outputs (lanes < LPR)
+    if (READS && tid < LPR) {
+        float y[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        float kap = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+                y[c] += red[w][tid][c];
+            kap += red[w][0][8];
+        }
+        if (OP == GDN) {
+            const float g = expf(gnew);
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+                y[c] *= g;
+        }
+        float rq[4] = {0.f, 0.f, 0.f, 0.f}, rk[4] = {0.f, 0.f, 0.f, 0.f};
+        if (LOGGED) {
+            if (STAGED)
                 kap = cf[2 * n];
-                for (int m = 0; m < n; ++m) {
-                    const float4 b = *reinterpret_cast<const float4 *>(Bt + m * T + 4 * c4);
-                    const float bs[4] = {b.x, b.y, b.z, b.w};
-                    const float cq = cf[m], ck = cf[n + m];
+            for (int m = 0; m < n; ++m) {
+                const float4 b = *reinterpret_cast<const float4 *>(Bt + m * T + 4 * c4);
+                const float bs[4] = {b.x, b.y, b.z, b.w};
+                const float cq = cf[m], ck = cf[n + m];
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        rq[c] = fmaf(cq, bs[c], rq[c]);
-                        if (DELTA)
-                            rk[c] = fmaf(ck, bs[c], rk[c]);
-                    }
+                for (int c = 0; c < 4; ++c) {
+                    rq[c] = fmaf(cq, bs[c], rq[c]);
+                    if (DELTA)
+                        rk[c] = fmaf(ck, bs[c], rk[c]);
                 }
             }
-            const float vs[4] = {vv.x, vv.y, vv.z, vv.w};
-            float bt[4], ov[4];
+        }
+        const float vs[4] = {vv.x, vv.y, vv.z, vv.w};
+        float bt[4], ov[4];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                if (DELTA) {
-                    bt[c] = bet * (vs[c] - y[4 + c] - rk[c]);
-                    ov[c] = y[c] + rq[c] + kap * bt[c];
-                } else {
-                    bt[c] = vs[c];
-                    ov[c] = y[c] + rq[c] + kap * vs[c];
-                }
+        for (int c = 0; c < 4; ++c) {
+            if (DELTA) {
+                bt[c] = bet * (vs[c] - y[4 + c] - rk[c]);
+                ov[c] = y[c] + rq[c] + kap * bt[c];
+            } else {
+                bt[c] = vs[c];
+                ov[c] = y[c] + rq[c] + kap * vs[c];
             }
-            *reinterpret_cast<float4 *>(a.o + (long)sh * DV + col) = make_float4(ov[0], ov[1], ov[2], ov[3]);
-            if (LOGGED) { // value-side append of entry n
-                const long off = ((long)sh * M + n) * DV + col;
-                if (DELTA) {
-                    *reinterpret_cast<float4 *>(static_cast<float *>(a.blog) + off) =
-                        make_float4(bt[0], bt[1], bt[2], bt[3]);
-                } else {
-                    const TIn *v = static_cast<const TIn *>(a.v) + (long)sh * DV + col;
-                    TIn *bl = static_cast<TIn *>(a.blog) + off;
+        }
+        *reinterpret_cast<float4 *>(a.o + (long)sh * DV + col) = make_float4(ov[0], ov[1], ov[2], ov[3]);
+        if (LOGGED && !MERGING) { // value-side append of entry n (a merge empties the log)
+            const long off = ((long)sh * M + n) * DV + col;
+            if (DELTA) {
+                *reinterpret_cast<float4 *>(static_cast<float *>(a.blog) + off) =
+                    make_float4(bt[0], bt[1], bt[2], bt[3]);
+            } else {
+                TIn *bl = static_cast<TIn *>(a.blog) + off;
 #pragma unroll
-                    for (int c = 0; c < 4; ++c)
-                        bl[c] = v[c];
-                }
+                for (int c = 0; c < 4; ++c)
+                    bl[c] = to_in<TIn>(vs[c]);
             }
-            if (WRITES)
-                *reinterpret_cast<float4 *>(Bt + (nb - 1) * T + 4 * c4) = make_float4(bt[0], bt[1], bt[2], bt[3]);
         }
         if (WRITES)
-            __syncthreads();
+            *reinterpret_cast<float4 *>(Bt + (nb - 1) * T + 4 * c4) = make_float4(bt[0], bt[1], bt[2], bt[3]);
     }
 
-    // 6. fold and write the tile once
+    // --------------------------------------- 7. fold and write the tile once
     if (WRITES) {
-        float gs = 1.f; // GDN: scalar base factor e^{Lam_f}
-        if (OP == GDN)
-            gs = expf(MODE == EAGER ? a.ld[sh] : MODE == FOLD ? L[n - 1] : L[n]);
+        __syncthreads();
+        const float gs = OP == GDN ? expf(gnew) : 1.f;
 #pragma unroll
         for (int p = 0; p < P; ++p) {
             const int r = r0 + p * RPP;
-            const float bf = OP == GDN ? gs : rowf[p];
+            const float bf = OP == GDN ? gs : Rf[r];
             float4 acc = make_float4(bf * x[p].x, bf * x[p].y, bf * x[p].z, bf * x[p].w);
             for (int m = 0; m < nf; ++m) {
                 const float f = F[m * DK + r];
@@ -433,7 +683,7 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void state_kernel(StepArgs a
                 acc.z = fmaf(f, b.z, acc.z);
                 acc.w = fmaf(f, b.w, acc.w);
             }
-            *reinterpret_cast<float4 *>(S + (long)r * DV + col) = acc;
+            buf_st4(tile_r, xoff, p * RPP * DV * 4, acc);
         }
     }
 }
@@ -466,56 +716,58 @@ hipError_t launch_prep(int dtype, int dk, const StepArgs &a, hipStream_t st)
 }
 
 template <int OP, typename TIn, int DK, int DV, int MODE>
-hipError_t launch_state_t(const StepArgs &a, hipStream_t st)
+hipError_t launch_step_t(const StepArgs &a, hipStream_t st)
 {
     using C = TileCfg<DK, DV>;
     const dim3 grid((unsigned)a.BH * C::NTILE);
     const size_t lds = sizeof(float) * (size_t)dyn_floats(MODE, a.n, DK, C::T);
-    hipLaunchKernelGGL((state_kernel<OP, TIn, DK, DV, MODE>), grid, dim3(C::NT), lds, st, a);
+    hipLaunchKernelGGL((step_kernel<OP, TIn, DK, DV, MODE>), grid, dim3(C::NT), lds, st, a);
     return hipGetLastError();
 }
 
 template <int OP, typename TIn, int DK, int DV>
-hipError_t launch_state_mode(int mode, const StepArgs &a, hipStream_t st)
+hipError_t launch_step_mode(int mode, const StepArgs &a, hipStream_t st)
 {
     switch (mode) {
-    case APPEND: return launch_state_t<OP, TIn, DK, DV, APPEND>(a, st);
-    case MERGE: return launch_state_t<OP, TIn, DK, DV, MERGE>(a, st);
-    case EAGER: return launch_state_t<OP, TIn, DK, DV, EAGER>(a, st);
-    case FOLD: return launch_state_t<OP, TIn, DK, DV, FOLD>(a, st);
+    case APPEND: return launch_step_t<OP, TIn, DK, DV, APPEND>(a, st);
+    case MERGE: return launch_step_t<OP, TIn, DK, DV, MERGE>(a, st);
+    case EAGER: return launch_step_t<OP, TIn, DK, DV, EAGER>(a, st);
+    case FOLD: return launch_step_t<OP, TIn, DK, DV, FOLD>(a, st);
+    case FAPPEND: return launch_step_t<OP, TIn, DK, DV, FAPPEND>(a, st);
+    case FMERGE: return launch_step_t<OP, TIn, DK, DV, FMERGE>(a, st);
     }
     return hipErrorInvalidValue;
 }
 
 template <int OP, typename TIn, int DK>
-hipError_t launch_state_dv(int dv, int mode, const StepArgs &a, hipStream_t st)
+hipError_t launch_step_dv(int dv, int mode, const StepArgs &a, hipStream_t st)
 {
     switch (dv) {
-    case 16: return launch_state_mode<OP, TIn, DK, 16>(mode, a, st);
-    case 32: return launch_state_mode<OP, TIn, DK, 32>(mode, a, st);
-    case 64: return launch_state_mode<OP, TIn, DK, 64>(mode, a, st);
-    case 128: return launch_state_mode<OP, TIn, DK, 128>(mode, a, st);
+    case 16: return launch_step_mode<OP, TIn, DK, 16>(mode, a, st);
+    case 32: return launch_step_mode<OP, TIn, DK, 32>(mode, a, st);
+    case 64: return launch_step_mode<OP, TIn, DK, 64>(mode, a, st);
+    case 128: return launch_step_mode<OP, TIn, DK, 128>(mode, a, st);
     }
     return hipErrorInvalidValue;
 }
 
 template <int OP, typename TIn>
-hipError_t launch_state_dk(int dk, int dv, int mode, const StepArgs &a, hipStream_t st)
+hipError_t launch_step_dk(int dk, int dv, int mode, const StepArgs &a, hipStream_t st)
 {
     switch (dk) {
-    case 16: return launch_state_dv<OP, TIn, 16>(dv, mode, a, st);
-    case 32: return launch_state_dv<OP, TIn, 32>(dv, mode, a, st);
-    case 64: return launch_state_dv<OP, TIn, 64>(dv, mode, a, st);
-    case 128: return launch_state_dv<OP, TIn, 128>(dv, mode, a, st);
+    case 16: return launch_step_dv<OP, TIn, 16>(dv, mode, a, st);
+    case 32: return launch_step_dv<OP, TIn, 32>(dv, mode, a, st);
+    case 64: return launch_step_dv<OP, TIn, 64>(dv, mode, a, st);
+    case 128: return launch_step_dv<OP, TIn, 128>(dv, mode, a, st);
     }
     return hipErrorInvalidValue;
 }
 
 template <int OP>
-hipError_t launch_state(int dtype, int dk, int dv, int mode, const StepArgs &a, hipStream_t st)
+hipError_t launch_step(int dtype, int dk, int dv, int mode, const StepArgs &a, hipStream_t st)
 {
-    return dtype == BF16 ? launch_state_dk<OP, uint16_t>(dk, dv, mode, a, st)
-                         : launch_state_dk<OP, float>(dk, dv, mode, a, st);
+    return dtype == BF16 ? launch_step_dk<OP, uint16_t>(dk, dv, mode, a, st)
+                         : launch_step_dk<OP, float>(dk, dv, mode, a, st);
 }
 
 } // namespace dl

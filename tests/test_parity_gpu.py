@@ -52,15 +52,16 @@ def test_serving_ops_reduced_batch(orc, wid):
 @pytest.mark.parametrize("op", ["gdn", "kda", "rwkv6"])
 @pytest.mark.parametrize("dk", [16, 32, 64, 128])
 @pytest.mark.parametrize("dv", [16, 32, 64, 128])
-def test_all_shapes(orc, op, dk, dv):
-    """Every supported (d_k, d_v) for every op, bf16 inputs, M=3, 7 steps
-    (two merges and a pending log), then a forced merge."""
+@pytest.mark.parametrize("path", ["fused", "staged"])
+def test_all_shapes(orc, op, dk, dv, path):
+    """Every supported (d_k, d_v) for every op and both paths, bf16 inputs,
+    M=3, 7 steps (two merges and a pending log), then a forced merge."""
     w = synth.Workload(9, op, 2, 3, dk, dv, 3, 7, "bf16")
     run = ParityRun(w, orc=orc)
     for _ in range(7):
-        run.step()
+        run.step(staged=path == "staged")
     run.merge()
-    _report(run, f"{op} dk={dk} dv={dv}")
+    _report(run, f"{op} dk={dk} dv={dv} {path}")
     run.close()
 
 
@@ -130,20 +131,40 @@ def test_m1_matches_eager_kernel(op):
 
 
 @needs_gpu
-def test_staged_calls_equal_decode_step():
-    """dl_replay_prep + dl_append_decode is bit-identical to dl_decode_step,
-    and two runs are bit-identical (no atomics, fixed reduction order)."""
-    w = synth.Workload(13, "kda", 2, 3, 128, 128, 4, 10, "bf16")
-    runs = [ParityRun(w) for _ in range(3)]
+@pytest.mark.parametrize("op", ["gdn", "kda", "rwkv6"])
+def test_staged_and_fused_paths(orc, op):
+    """The two-stage path (dl_replay_prep + dl_append_decode) and the one-launch
+    path (dl_decode_step) both match the oracle and each other; repeated runs
+    of one path are bit-identical (no atomics, fixed reduction order)."""
+    w = synth.Workload(13, op, 2, 3, 128, 128, 4, 10, "bf16")
+    fused = [ParityRun(w, orc=orc) for _ in range(2)]
+    staged = [ParityRun(w, orc=orc) for _ in range(2)]
     for t in range(10):
         s = synth.step(w, t)
-        runs[0].step(s)
-        runs[1].step(s, staged=True)
-        runs[2].step(s)
-    g = [r.state_gpu() for r in runs]
-    assert np.array_equal(g[0], g[1]) and np.array_equal(g[0], g[2])
-    for r in runs:
+        for r in fused:
+            r.step(s)
+        for r in staged:
+            r.step(s, staged=True)
+    g = [r.state_gpu() for r in fused + staged]
+    assert np.array_equal(g[0], g[1]) and np.array_equal(g[2], g[3])
+    assert rel(g[0], g[2]) < 1e-5
+    for r in fused + staged:
+        _report(r, f"{op} {'staged' if r in staged else 'fused'}")
         r.close()
+
+
+@needs_gpu
+@pytest.mark.parametrize("op", ["gdn", "kda", "rwkv6"])
+@pytest.mark.parametrize("M", [3, 8, 32])
+def test_staged_path_merge_intervals(orc, op, M):
+    """The two-stage ReplayPrep/AppendDecode path over whole merge cycles."""
+    w = synth.Workload(16, op, 3, 5, 64, 128, M, 2 * M + 1, "bf16")
+    run = ParityRun(w, orc=orc)
+    for _ in range(w.steps):
+        run.step(staged=True)
+    run.merge()
+    _report(run, f"{op} staged M={M}")
+    run.close()
 
 
 @needs_gpu
