@@ -1,21 +1,26 @@
 """Benchmark of the DeltaLog decode step on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload 1] [--rotate R] ...
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1] [--rotate R] ...
 
-One "step" is one DeltaLog decode step (ReplayPrep + AppendDecode, with the
-fused merge on every M-th step) for all B*H slot-heads of one state, inputs
-already resident in HBM.  With --rotate R the steps go round R independent
-states (like R layers), so the working set exceeds the 256 MB Infinity Cache
-and the state really streams from HBM; the default R=4 is used for the
-headline value.  Prints ONE JSON line (rank 0) with the throughput in
-(token*head)/s, the roofline of the dominant kernel (the state kernel:
-AppendDecode + fused merge) measured with HIP events on the launch stream,
-the same-GPU eager baseline, and the fp64 CPU oracle timed on a bounded
-sample.
+One "step" is one DeltaLog decode step (dl_decode_step: one launch of the
+step kernel, which also folds the log into the base on every M-th step) for
+all B*H slot-heads of one state, with its inputs already resident in HBM.
+The default workload is GDN B=64 H=32 d_k=d_v=128 M=8 with bf16 q/k/v and an
+fp32 state.  With --rotate R (default 4) the steps go round R independent
+states, as the layers of a model do, so the 512 MiB working set exceeds the
+256 MB Infinity Cache and the state streams from HBM as in serving; the
+single-state figure (cache-resident) is reported beside it.
+
+Prints ONE JSON line with the throughput in (token*head)/s, the roofline of
+the step kernel (algorithmic bytes per launch / mean launch time measured
+with HIP events on the launch stream), the same-GPU eager and two-stage
+figures, the other operators' workloads, and the fp64 CPU oracle timed on a
+bounded sample.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -28,6 +33,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "state-update (token·head)/s + achieved HBM GB/s vs peak, GDN B=64 H=32 d=128"
 PEAK_HBM_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "recurrent_state_update_amd", "csrc", "dl_kernels.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "step_kernel_traffic.json")
 
 
 def log(*a):
@@ -35,49 +42,48 @@ def log(*a):
 
 
 # --------------------------------------------------------------- byte model --
-def state_kernel_bytes(w, n: int, mode: str) -> int:
-    """Algorithmic HBM bytes of one launch of the state kernel over all B*H
-    slot-heads: the unique bytes the step must move by its definition.
-    mode: 'append' | 'merge' (n = log entries before the step) | 'eager'."""
-    dk, dv = w.dk, w.dv
+def _sizes(w):
     es = 2 if w.dtype == "bf16" else 4
     delta = w.op != "rwkv6"
-    bsz = 4 if delta else es
-    lsz = 4 if w.op == "gdn" else 4 * dk
-    P = 4 * dk * dv
-    io = dv * es + dv * 4 + (4 if delta else 0)           # v, o, beta
-    if mode == "eager":
-        per = 2 * P + io + (2 * dk * es) + lsz + (0 if delta else 4 * dk)  # + q,k, decay, u
-        return per * w.BH
-    per = P + io
-    per += (2 * dk * es) if delta else dk * es             # q,k (RWKV6: r only)
-    per += n * dv * bsz                                    # value-side log shard
-    per += (2 * n + 1) * 4 if delta else (n + 1) * 4       # replay coefficients
-    per += dv * bsz                                        # append b_t
-    if w.op == "kda":
-        per += lsz                                         # Lambda'
-    elif w.op == "rwkv6":
-        per += (lsz if n > 0 else 0)                       # Lambda_{n-1}
+    return dict(P=4 * w.dk * w.dv, es=es, delta=delta, bsz=4 if delta else es,
+                lsz=4 if w.op == "gdn" else 4 * w.dk)
+
+
+def step_launch_bytes(w, n: int, merge: bool) -> int:
+    """Algorithmic HBM bytes of one launch of the one-launch step kernel over
+    all B*H slot-heads, n = log entries before the step.  Per slot-head:
+    base read P (+ base write P on a merge); the n logged entries' a_j, Lam_j
+    and b_j; q, k, v, beta, log-decay (+ u for RWKV6); o; and on append steps
+    the appended a_n, Lam_n, b_n."""
+    z = _sizes(w)
+    dk, dv = w.dk, w.dv
+    per = z["P"] + n * (dk * z["es"] + z["lsz"] + dv * z["bsz"])
+    per += 2 * dk * z["es"] + dv * z["es"] + (4 if z["delta"] else 4 * dk) + z["lsz"]
+    per += dv * 4
+    if merge:
+        per += z["P"]
     else:
-        per += 4
-    if mode == "merge":
-        per += P                                           # the one dense write
-        per += n * dk * es + n * lsz                       # a_j, Lambda_j of logged entries
-        if w.op == "rwkv6":
-            per += lsz                                     # Lambda' for the fold
+        per += dk * z["es"] + z["lsz"] + dv * z["bsz"]
+    return per * w.BH
+
+
+def eager_launch_bytes(w) -> int:
+    """Eager step: read and write the base, inputs, o."""
+    z = _sizes(w)
+    per = 2 * z["P"] + 2 * w.dk * z["es"] + w.dv * z["es"] + z["lsz"] + w.dv * 4
+    per += 4 if z["delta"] else 4 * w.dk
     return per * w.BH
 
 
 def modelled_step_bytes(w) -> float:
-    """Whole-step bytes (both kernels) averaged over an M-cycle, SURVEY-style
-    model: P(1+1/M) + E((M-1)/M + (M-1)/2) + I, per slot-head."""
-    dk, dv, M = w.dk, w.dv, w.M
-    es = 2 if w.dtype == "bf16" else 4
-    delta = w.op != "rwkv6"
-    P = 4 * dk * dv
-    E = dk * es + (dv * 4 if delta else dv * es) + (4 if w.op == "gdn" else 4 * dk)
-    I = 2 * dk * es + dv * es + dv * 4 + (8 if w.op == "gdn" else 4 + 4 * dk)
-    return (P * (1 + 1 / M) + E * ((M - 1) / M + (M - 1) / 2) + I) * w.BH
+    """Per-step bytes of the method averaged over an M-cycle (one launch per
+    step): P(1 + 1/M) + E((M-1)/M + (M-1)/2) + I per slot-head, E the bytes of
+    one log entry, I the step's inputs and outputs."""
+    z = _sizes(w)
+    M = w.M
+    E = w.dk * z["es"] + w.dv * z["bsz"] + z["lsz"]
+    I = 2 * w.dk * z["es"] + w.dv * z["es"] + w.dv * 4 + z["lsz"] + (4 if z["delta"] else 4 * w.dk)
+    return (z["P"] * (1 + 1 / M) + E * ((M - 1) / M + (M - 1) / 2) + I) * w.BH
 
 
 # ------------------------------------------------------------------- setup --
@@ -89,11 +95,8 @@ def stage_inputs(w, pool: int, dt):
     d = synth.steps(w, 0, pool)
     out = {}
     for key, a in d.items():
-        if a is None:
-            out[key] = None
-            continue
-        tdt = dt if key in ("q", "k", "v") else torch.float32
-        out[key] = torch.from_numpy(a).to("cuda").to(tdt).contiguous()
+        out[key] = None if a is None else torch.from_numpy(a).to("cuda").to(
+            dt if key in ("q", "k", "v") else torch.float32).contiguous()
     log(f"staged {pool} steps of inputs for {w.describe()} in {time.time() - t0:.1f}s")
     return out
 
@@ -110,17 +113,17 @@ def make_states(w, R: int, dt):
     return sts, base0, u_dev
 
 
-# ------------------------------------------------------------------- timing --
 def _ptrs(inp, s):
-    """Raw device addresses of step s's inputs (so the timed loop does no
-    tensor indexing)."""
     g = lambda key: None if inp[key] is None else inp[key][s].data_ptr()
     return g("q"), g("k"), g("v"), g("beta"), g("ld")
 
 
-def run_deltalog(w, inp, sts, K: int, W: int, instrument: bool):
-    """W warm-up + K timed steps, state i % R at step i.  Returns wall ms,
-    per-launch state-kernel ms (list of (ms, n, mode)) and ReplayPrep ms."""
+# ------------------------------------------------------------------- timing --
+def run_deltalog(w, inp, sts, K: int, W: int, instrument: bool, path: str = "fused"):
+    """W warm-up + K timed steps on state i % R.  Returns wall ms and, when
+    instrumented, per-launch kernel ms as (ms, n, merge) for the step kernel
+    plus the ReplayPrep ms (two-stage path).  The timed loop passes raw device
+    addresses straight to the C ABI."""
     import torch
     import recurrent_state_update_amd as rsu
     stream = torch.cuda.current_stream()
@@ -131,25 +134,33 @@ def run_deltalog(w, inp, sts, K: int, W: int, instrument: bool):
     outs = [torch.empty(w.B, w.H, w.dv, device="cuda") for _ in range(2)]
     optr = [o.data_ptr() for o in outs]
     hs = [st._h for st in sts]
-    prep_f, app_f = rsu._lib.dl_replay_prep, rsu._lib.dl_append_decode
+    L = rsu._lib
 
     def one(i, evs=None):
         h = hs[i % R]
         q, k, v, beta, ld = ptrs[i % pool]
-        if evs is not None:
-            evs[0].record(stream)
-        if prep_f(h, q, k, ld, sp) != 0:
-            raise RuntimeError("dl_replay_prep failed")
-        if evs is not None:
-            evs[1].record(stream)
-        if app_f(h, q, k, v, beta, optr[i % 2], sp) != 0:
-            raise RuntimeError("dl_append_decode failed")
-        if evs is not None:
-            evs[2].record(stream)
+        if path == "fused":
+            if evs is not None:
+                evs[0].record(stream)
+            st = L.dl_decode_step(h, q, k, v, beta, ld, optr[i % 2], sp)
+            if evs is not None:
+                evs[1].record(stream)
+        else:
+            if evs is not None:
+                evs[0].record(stream)
+            st = L.dl_replay_prep(h, q, k, ld, sp)
+            if evs is not None:
+                evs[2].record(stream)
+            st = st or L.dl_append_decode(h, q, k, v, beta, optr[i % 2], sp)
+            if evs is not None:
+                evs[1].record(stream)
+        if st != 0:
+            raise RuntimeError(f"DeltaLog step failed: {rsu.dl_status_string(st)}")
 
     for i in range(W):
         one(i)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)] if instrument else None
+    nev = 3 if path != "fused" else 2
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(K)] if instrument else None
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     ns = []
@@ -164,10 +175,12 @@ def run_deltalog(w, inp, sts, K: int, W: int, instrument: bool):
     launches, prep = [], []
     if instrument:
         for i in range(K):
-            n = ns[i]
-            mode = "merge" if n + 1 == w.M else "append"
-            launches.append((evs[i][1].elapsed_time(evs[i][2]), n, mode))
-            prep.append(evs[i][0].elapsed_time(evs[i][1]))
+            merge = ns[i] + 1 == w.M
+            if path == "fused":
+                launches.append((evs[i][0].elapsed_time(evs[i][1]), ns[i], merge))
+            else:
+                launches.append((evs[i][2].elapsed_time(evs[i][1]), ns[i], merge))
+                prep.append(evs[i][0].elapsed_time(evs[i][2]))
     return wall, launches, prep
 
 
@@ -206,31 +219,121 @@ def run_eager(w, inp, bases, u_dev, K: int, W: int, instrument: bool):
         one(W + i, evs[i] if instrument else None)
     t1.record(stream)
     torch.cuda.synchronize()
-    wall = t0.elapsed_time(t1)
     per = [evs[i][0].elapsed_time(evs[i][1]) for i in range(K)] if instrument else []
-    return wall, per
+    return t0.elapsed_time(t1), per
 
 
-def cpu_baseline(w, budget_s: float = 12.0, max_steps: int = 64):
+def cpu_baseline(w, budget_s=(8.0, 5.0), pool: int = 32):
     """The fp64 oracle's eager recurrence on the host cores, over all B*H
-    slot-heads of the workload, for as many of its steps as fit the budget."""
+    slot-heads of the workload: the first `pool` steps' inputs are generated
+    once (not timed) and stepped through repeatedly until the time budget is
+    spent, first with all OpenMP threads, then with one."""
     import synth
     from oracle import Oracle
     orc = Oracle()
     X0, u = synth.initial(w)
-    X = X0.astype(np.float64)
-    done, spent = 0, 0.0
-    while done < max_steps and spent < budget_s:
-        s = synth.step(w, done)
-        args = [None if s[k] is None else s[k].astype(np.float64) for k in ("q", "k", "v", "beta", "ld")]
-        t0 = time.perf_counter()
-        orc.eager_step(w.op, X, *args, None if u is None else u.astype(np.float64))
-        spent += time.perf_counter() - t0
-        done += 1
-    return dict(value=w.BH * done / spent, unit="(token·head)/s", cores=orc.max_threads(),
-                kind="oracle",
-                sample=f"fp64 eager oracle, all {w.BH} slot-heads of {w.describe()}, first {done} "
-                       f"steps ({spent:.1f} s of compute, input generation excluded)")
+    uu = None if u is None else u.astype(np.float64)
+    steps = []
+    for s_ in range(min(pool, w.steps)):
+        s = synth.step(w, s_)
+        steps.append([None if s[k] is None else s[k].astype(np.float64) for k in ("q", "k", "v", "beta", "ld")])
+    threads = orc.max_threads()
+    out = {}
+    for nthr, budget in zip((threads, 1), budget_s):
+        orc.set_threads(nthr)
+        X = X0.astype(np.float64)
+        done, spent = 0, 0.0
+        while spent < budget:
+            t0 = time.perf_counter()
+            orc.eager_step(w.op, X, *steps[done % len(steps)], uu)
+            spent += time.perf_counter() - t0
+            done += 1
+        out[nthr] = (w.BH * done / spent, done, spent)
+    orc.set_threads(threads)
+    v, done, spent = out[threads]
+    v1, done1, spent1 = out[1]
+    return dict(value=round(v, 1), unit="(token·head)/s", cores=threads, kind="oracle",
+                sample=f"fp64 eager oracle over all {w.BH} slot-heads of {w.describe()}, cycling its "
+                       f"first {len(steps)} steps' inputs: {done} steps on {threads} threads in "
+                       f"{spent:.1f} s; on 1 thread {round(v1, 1)} (token·head)/s ({done1} steps in "
+                       f"{spent1:.1f} s); input generation not timed")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the step kernel from the committed rocprofv3
+    counter summary, if it was taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        with open(KERNEL_SRC, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != sha:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def bench_workload(w, K, W, R, pool, with_eager=True, with_staged=True):
+    """Time workload w.  The timed region holds only K back-to-back launches of
+    the step kernel (one per step, HIP events at its two ends on the launch
+    stream): its length / K is both the step time and the kernel's mean launch
+    duration (dispatch gaps included).  A second, per-launch event-bracketed
+    pass splits append and merge launches (each bracket adds event overhead)."""
+    import torch
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    inp = stage_inputs(w, pool, dt)
+    sts, base0, u_dev = make_states(w, R, dt)
+    res = {}
+    ns0 = [st.log_len for st in sts]
+    wall, _, _ = run_deltalog(w, inp, sts, K, W, instrument=False, path="fused")
+    # log length seen by each timed launch (the schedule is deterministic)
+    ns = []
+    cur = list(ns0)
+    for i in range(W + K):
+        r = i % R
+        if i >= W:
+            ns.append(cur[r])
+        cur[r] = 0 if cur[r] + 1 == w.M else cur[r] + 1
+    tot_bytes = sum(step_launch_bytes(w, n, n + 1 == w.M) for n in ns)
+    avg_ms = wall / K
+    res["wall_ms"] = wall
+    res["value"] = w.BH * K / (wall * 1e-3)
+    achieved = tot_bytes / K / (avg_ms * 1e-3) / 1e9
+    res["roofline"] = dict(
+        bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+        frac=round(achieved / PEAK_HBM_GBS, 4), traffic=None,
+        kernel="step_kernel, one-launch append/merge modes (dl_decode_step)",
+        avg_launch_us=round(avg_ms * 1e3, 2), bytes_per_launch=int(tot_bytes / K))
+    _, launches, _ = run_deltalog(w, inp, sts, K, W, instrument=True, path="fused")
+    app = [x[0] for x in launches if not x[2]]
+    mer = [x[0] for x in launches if x[2]]
+    res["roofline"]["event_bracketed_us"] = dict(append=round(1e3 * sum(app) / max(len(app), 1), 2),
+                                                 merge=round(1e3 * sum(mer) / max(len(mer), 1), 2))
+    res["modelled_step_GBs"] = round(modelled_step_bytes(w) / (avg_ms * 1e-3) / 1e9, 1)
+    if R > 1:
+        one, _, _ = run_deltalog(w, inp, sts[:1], K, W, instrument=False)
+        res["single_state_value"] = round(w.BH * K / (one * 1e-3), 1)
+    if with_staged:
+        sw, _, _ = run_deltalog(w, inp, sts, K, W, instrument=False, path="staged")
+        _, sl, sp = run_deltalog(w, inp, sts, K, W, instrument=True, path="staged")
+        res["two_stage"] = dict(value=round(w.BH * K / (sw * 1e-3), 1), ms_per_step=round(sw / K, 5),
+                                event_bracketed_us=dict(
+                                    append_decode=round(1e3 * sum(x[0] for x in sl) / len(sl), 2),
+                                    replay_prep=round(1e3 * sum(sp) / len(sp), 2)))
+    if with_eager:
+        bases = [base0.clone() for _ in range(R)]
+        ew, _ = run_eager(w, inp, bases, u_dev, K, W, instrument=False)
+        eavg = ew / K
+        res["eager_same_gpu"] = dict(
+            value=round(w.BH * K / (ew * 1e-3), 1), ms_per_step=round(eavg, 5),
+            achieved_GBs=round(eager_launch_bytes(w) / (eavg * 1e-3) / 1e9, 1),
+            deltalog_speedup=round(ew / wall, 3))
+    for st in sts:
+        st.close()
+    del inp, sts
+    torch.cuda.empty_cache()
+    return res
 
 
 # -------------------------------------------------------------------- main --
@@ -240,20 +343,21 @@ def main():
     ap.add_argument("--steps", type=int, default=512)
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--workload", type=int, default=1, choices=[1, 2, 3, 4])
-    ap.add_argument("--op", default=None, help="op for workload 4 (gdn|kda)")
-    ap.add_argument("--M", type=int, default=None, help="merge interval override (workload 4)")
+    ap.add_argument("--op", default=None, help="operator of workload 4 (gdn|kda)")
+    ap.add_argument("--M", type=int, default=None, help="merge interval (workload 4 sweep)")
     ap.add_argument("--rotate", type=int, default=4, help="independent states stepped in turn")
     ap.add_argument("--pool", type=int, default=None, help="distinct input steps staged")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--no-eager", action="store_true")
-    ap.add_argument("--separate-instrument", action="store_true",
-                    help="time the per-kernel events in a second pass instead of the timed one")
+    ap.add_argument("--no-others", action="store_true", help="skip the KDA / RWKV6 workloads")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB, 10 times (the "
+                         "reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the DeltaLog decode step needs no exchange "
-              "between GPUs (slot-heads shard with zero communication); run with --gpus 1.",
-              file=sys.stderr)
+        print("bench.py measures one GPU: the DeltaLog decode step needs no exchange between "
+              "GPUs (slot-heads shard with zero communication), so there is no multi-GPU "
+              "figure to take; run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -261,91 +365,80 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
 
+    if args.calibrate_copy:
+        n = args.calibrate_copy * 2**20 // 4
+        src = torch.ones(n, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(10):
+            dst.copy_(src)
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / 10
+        print(json.dumps({"calibrate_copy_bytes_read": n * 4, "calibrate_copy_bytes_written": n * 4,
+                          "dispatches": 10, "copy_GBs_read_plus_write": round(2 * n * 4 / ms / 1e6, 1)}),
+              flush=True)
+        return
+
     if args.workload == 4:
         w = synth.sweep_workload(args.op or "gdn", args.M or 8)
     else:
         w = synth.WORKLOADS[args.workload]
         if args.M:
             w = w.with_(M=args.M)
-    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     K, W, R = args.steps, args.warmup, args.rotate
-    pool = args.pool or min(w.steps, 256 if w.B <= 64 else 64)
-    inp = stage_inputs(w, pool, dt)
-    sts, base0, u_dev = make_states(w, R, dt)
+    pool = args.pool or min(w.steps, 256 if w.B <= 128 else 64)
+    res = bench_workload(w, K, W, R, pool)
+    traffic = measured_traffic() if (args.workload == 1 and not args.M) else None
+    res["roofline"]["traffic"] = traffic
+    log(f"{w.describe()}: {res['wall_ms'] / K * 1e3:.2f} us/step")
 
-    inst_in_timed = not args.separate_instrument
-    wall, launches, prep = run_deltalog(w, inp, sts, K, W, instrument=inst_in_timed)
-    if not inst_in_timed:
-        _, launches, prep = run_deltalog(w, inp, sts, K, W, instrument=True)
-    wall_pure, _, _ = run_deltalog(w, inp, sts, K, W, instrument=False)
-    log(f"deltalog: {K} steps in {wall:.3f} ms (instrumented), {wall_pure:.3f} ms (no per-kernel events)")
-
-    tot_ms = sum(x[0] for x in launches)
-    tot_bytes = sum(state_kernel_bytes(w, n, mode) for (_, n, mode) in launches)
-    achieved = tot_bytes / (tot_ms * 1e-3) / 1e9
-    avg_ms = tot_ms / len(launches)
-    app = [x[0] for x in launches if x[2] == "append"]
-    mer = [x[0] for x in launches if x[2] == "merge"]
-    roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
-                    frac=round(achieved / PEAK_HBM_GBS, 4), traffic=None,
-                    kernel="state_kernel (AppendDecode + fused merge)",
-                    avg_launch_us=round(avg_ms * 1e3, 2),
-                    append_us=round(1e3 * sum(app) / max(len(app), 1), 2),
-                    merge_us=round(1e3 * sum(mer) / max(len(mer), 1), 2),
-                    bytes_per_launch=int(tot_bytes / len(launches)))
-
-    value = w.BH * K / (wall_pure * 1e-3)
-    extra = dict(
-        rotate_states=R,
-        prep_avg_us=round(1e3 * sum(prep) / max(len(prep), 1), 2),
-        modelled_step_GBs=round(modelled_step_bytes(w) / (wall_pure / K * 1e-3) / 1e9, 1),
-    )
-
-    if not args.no_eager:
-        bases = [base0.clone() for _ in range(R)]
-        e_wall, e_per = run_eager(w, inp, bases, u_dev, K, W, instrument=True)
-        e_pure, _ = run_eager(w, inp, bases, u_dev, K, W, instrument=False)
-        e_bytes = state_kernel_bytes(w, 0, "eager")
-        e_avg = sum(e_per) / len(e_per)
-        extra["eager_same_gpu"] = dict(
-            value=round(w.BH * K / (e_pure * 1e-3), 1), ms_per_step=round(e_pure / K, 5),
-            avg_launch_us=round(e_avg * 1e3, 2),
-            achieved_GBs=round(e_bytes / (e_avg * 1e-3) / 1e9, 1),
-            speedup_deltalog=round(e_pure / wall_pure, 3))
-        log(f"eager: {K} steps in {e_pure:.3f} ms")
-
-    # single state (fits the Infinity Cache) for context
-    if R > 1:
-        one, _, _ = run_deltalog(w, inp, sts[:1], K, W, instrument=False)
-        extra["single_state_value"] = round(w.BH * K / (one * 1e-3), 1)
+    others = {}
+    if not args.no_others and args.workload == 1:
+        for wid in (2, 3):
+            o = synth.WORKLOADS[wid]
+            r = bench_workload(o, K, W, R, min(o.steps, 256), with_staged=False)
+            others[o.op] = dict(workload=o.describe(), value=round(r["value"], 1),
+                                ms_per_step=round(r["wall_ms"] / K, 5),
+                                achieved_GBs=r["roofline"]["achieved"], frac=r["roofline"]["frac"],
+                                eager_value=r["eager_same_gpu"]["value"],
+                                deltalog_speedup=r["eager_same_gpu"]["deltalog_speedup"])
+            log(f"{o.describe()}: {r['wall_ms'] / K * 1e3:.2f} us/step")
 
     cpu = None
     if not args.no_cpu:
         log("timing the CPU oracle ...")
         cpu = cpu_baseline(w)
 
-    res = {
+    out = {
         "metric": METRIC,
-        "value": round(value, 1),
+        "value": round(res["value"], 1),
         "unit": "(token·head)/s",
         "n_gpus": 1,
         "steps": K,
         "warmup": W,
-        "ms_per_step": round(wall_pure / K, 5),
+        "ms_per_step": round(res["wall_ms"] / K, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
-        "data": "synthetic (seeded PCG64; bf16 q/k/v, fp32 state/beta/decay)",
-        "config": {"workload": f"DeltaLog {w.op.upper()} decode B={w.B} H={w.H} d_k={w.dk} "
-                               f"d_v={w.dv} M={w.M}, {R} states stepped in turn",
+        "data": "synthetic (seeded PCG64; bf16 q/k/v, fp32 state, beta and log-decay)",
+        "config": {"workload": f"DeltaLog {w.op.upper()} decode step, B={w.B} H={w.H} "
+                               f"d_k={w.dk} d_v={w.dv} M={w.M}, {R} states stepped in turn",
                    "B": w.B, "H": w.H, "d_k": w.dk, "d_v": w.dv, "M": w.M, "op": w.op,
                    "rotate_states": R, "input_pool_steps": pool},
-        "roofline": roofline,
+        "roofline": res["roofline"],
         "cpu_baseline": cpu,
-        **extra,
+        "modelled_step_GBs": res["modelled_step_GBs"],
+        "single_state_value": res.get("single_state_value"),
+        "two_stage": res.get("two_stage"),
+        "eager_same_gpu": res.get("eager_same_gpu"),
+        "other_workloads": others or None,
     }
-    print(json.dumps(res), flush=True)
+    print(json.dumps(out), flush=True)
 
 
 if __name__ == "__main__":

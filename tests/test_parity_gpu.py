@@ -213,3 +213,37 @@ def test_checkpoint_restore_mid_cycle(op):
     a.merge()
     b.merge()
     assert torch.equal(a.base, b.base)
+
+
+@needs_gpu
+@pytest.mark.parametrize("wid", [1, 2, 3])
+def test_full_size_workloads(orc, wid):
+    """Workloads 1-3 at full size (B*H slot-heads, all 256 steps, the
+    one-launch path the benchmark times).  Slot-heads are independent, so the
+    oracle follows a deterministic sample of 48 of them (first and last
+    included): o every step and the base after every merge."""
+    w = synth.WORKLOADS[wid]
+    idx = sample_slot_heads(w.BH, 48, seed=wid)
+    run = ParityRun(w, idx=idx, orc=orc)
+    for _ in range(w.steps):
+        run.step()
+    assert run.checked_S == w.steps // w.M
+    _report(run, f"w{wid} full size")
+    run.close()
+
+
+@needs_gpu
+@pytest.mark.parametrize("op", ["gdn", "kda"])
+@pytest.mark.parametrize("M", [1, 2, 4, 8, 16])
+def test_large_batch_sweep_sizes(orc, op, M):
+    """The large-batch sweep shape (B=256 H=32 d=128, 512 MiB state) at each
+    merge interval: 32 steps (whole cycles for every M), 32 sampled
+    slot-heads, then a forced merge."""
+    w = synth.sweep_workload(op, M, steps=32)
+    idx = sample_slot_heads(w.BH, 32, seed=M)
+    run = ParityRun(w, idx=idx, orc=orc)
+    for _ in range(w.steps):
+        run.step()
+    run.merge()
+    _report(run, f"{op} B=256 M={M}")
+    run.close()
