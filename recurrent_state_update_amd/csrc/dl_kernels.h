@@ -36,7 +36,7 @@
 // bounds-limited buffer resource: they return zero without touching memory,
 // which keeps the code branch-free (no load gets sunk behind a wait) and adds
 // no traffic.  Column sums reduce across lanes with xor-shuffles and across
-// waves through LDS.  Workgroups of one slot-head are placed on the same XCD.
+// waves through LDS.
 #pragma once
 
 #include "dl_internal.h"
@@ -62,18 +62,6 @@ template <int FROM> __device__ __forceinline__ float wave_sum_from(float x)
     for (int off = FROM; off < 64; off <<= 1)
         x += __shfl_xor(x, off, 64);
     return x;
-}
-
-// Workgroup b of a 1-D grid is dispatched to XCD b % 8.  Renumber so each XCD
-// works on a contiguous range of logical tiles (tiles of one slot-head then
-// share that XCD's L2 for their common metadata).  Bijective on [0, G).
-__device__ __forceinline__ int xcd_remap(int b, int G)
-{
-    constexpr int NX = 8;
-    const int per = G / NX;
-    if (b >= per * NX)
-        return b;
-    return (b % NX) * per + b / NX;
 }
 
 // Raw buffer resources: a base, a size in bytes, and loads at a 32-bit byte
@@ -132,6 +120,46 @@ template <> __device__ __forceinline__ float to_in<float>(float x) { return x; }
 template <> __device__ __forceinline__ uint16_t to_in<uint16_t>(float x)
 {
     return static_cast<uint16_t>(__float_as_uint(x) >> 16);
+}
+
+// Raw forms of the element loads: the bits are returned untouched and
+// converted later, so a load inside a branch does not force a wait there
+// (a conversion next to the load would).
+// Raw bits of one element, always as a 32-bit word: fp32 loads the element;
+// bf16 loads the aligned word that holds it (two adjacent lanes share a word,
+// so the access stays coalesced) and cvt1 picks the half from the element
+// index's parity.  Keeping 32-bit raw words means no zero-extension or
+// packing has to sit next to the load.
+template <typename TIn> __device__ __forceinline__ unsigned buf_raw1(rsrc_t r, unsigned e)
+{
+    if constexpr (sizeof(TIn) == 4)
+        return __builtin_amdgcn_raw_buffer_load_b32(r, e * 4u, 0, 0);
+    else
+        return __builtin_amdgcn_raw_buffer_load_b32(r, (e & ~1u) * 2u, 0, 0);
+}
+template <typename TIn> __device__ __forceinline__ float cvt1(unsigned raw, unsigned e)
+{
+    if constexpr (sizeof(TIn) == 4)
+        return __uint_as_float(raw);
+    else
+        return __uint_as_float((e & 1u) ? (raw & 0xffff0000u) : (raw << 16));
+}
+template <typename TIn> __device__ __forceinline__ u32x4 buf_raw4(rsrc_t r, unsigned e)
+{
+    if constexpr (sizeof(TIn) == 4) {
+        return __builtin_amdgcn_raw_buffer_load_b128(r, e * 4u, 0, 0);
+    } else {
+        const u32x2 h = __builtin_amdgcn_raw_buffer_load_b64(r, e * 2u, 0, 0);
+        return u32x4{h[0], h[1], 0u, 0u};
+    }
+}
+template <typename TIn> __device__ __forceinline__ float4 cvt4(u32x4 raw)
+{
+    if constexpr (sizeof(TIn) == 4)
+        return __builtin_bit_cast(float4, raw);
+    else
+        return make_float4(__uint_as_float(raw[0] << 16), __uint_as_float(raw[0] & 0xffff0000u),
+                           __uint_as_float(raw[1] << 16), __uint_as_float(raw[1] & 0xffff0000u));
 }
 
 template <int DK, int DV> struct TileCfg {
@@ -329,8 +357,10 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int c4 = tid % LPR, r0 = tid / LPR;
-    const int blk = xcd_remap(blockIdx.x, gridDim.x);
-    const int sh = blk / NTILE, tile = blk % NTILE;
+    // Natural block order: consecutive workgroups (dispatched round-robin over
+    // the 8 XCDs) read adjacent tiles, which streams HBM faster than giving
+    // each XCD a contiguous slab of the state (measured).
+    const int sh = blockIdx.x / NTILE, tile = blockIdx.x % NTILE;
     const int col = tile * T + 4 * c4;
     const int M = a.M, n = a.n;
 
@@ -360,22 +390,34 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
     const rsrc_t ld_r = make_rsrc(a.ld + (OP == GDN ? sh : (long)sh * DK),
                                   (MODE == EAGER || FUSED) ? (OP == GDN ? 1 : DK) * 4 : 0);
     const rsrc_t u_r = make_rsrc(a.u + (long)(sh % a.H) * DK, (OP == RWKV6 && KAPPA_HERE) ? DK * 4 : 0);
-    float mq[RW], mk[RW], mprev[RW], mcur[RW], mell[RW], mu[RW];
+    // Loads are skipped outright (wave-uniform branches) where a whole wave
+    // needs none of them, and pointed past the resource end where only some
+    // of its lanes do.
+    unsigned rq_[RW], rk_[RW], rprev[RW], rcur[RW], rell[RW], ru[RW]; // raw words
 #pragma unroll
     for (int j = 0; j < RW; ++j) {
         const int i = tid + j * NT;
         const unsigned ei = i < DK ? (unsigned)i : kSkipElem;
-        mq[j] = buf_ld_in<TIn>(q_r, ei);
-        mk[j] = buf_ld_in<TIn>(k_r, ei);
-        // per-key log-decays: Lam_{n-1} (0 when the log is empty), Lam_n, ell_t
-        mprev[j] = mcur[j] = mell[j] = 0.f;
-        if (OP != GDN) {
-            mprev[j] = buf_ld_in<float>(L_r, (n > 0 && i < DK) ? (unsigned)((n - 1) * DK + i) : kSkipElem);
-            if (STAGED)
-                mcur[j] = buf_ld_in<float>(L_r, i < DK ? (unsigned)(n * DK + i) : kSkipElem);
-            mell[j] = buf_ld_in<float>(ld_r, ei);
+        // skipped loads leave an unused, non-constant placeholder (a constant
+        // would let the compiler fold the later conversion into the branch)
+        rq_[j] = rk_[j] = rprev[j] = rcur[j] = rell[j] = ru[j] = (unsigned)tid;
+        if (wave * 64 + j * NT < DK) { // this wave holds rows of the tables
+            if (READS) {
+                rq_[j] = buf_raw1<TIn>(q_r, ei);
+                rk_[j] = buf_raw1<TIn>(k_r, ei);
+            }
+            // per-key log-decays: Lam_{n-1} (0 when the log is empty), Lam_n, ell_t
+            if (OP != GDN) {
+                if (n > 0 && MODE != EAGER)
+                    rprev[j] = buf_raw1<float>(L_r, i < DK ? (unsigned)((n - 1) * DK + i) : kSkipElem);
+                if (STAGED)
+                    rcur[j] = buf_raw1<float>(L_r, i < DK ? (unsigned)(n * DK + i) : kSkipElem);
+                if (MODE == EAGER || FUSED)
+                    rell[j] = buf_raw1<float>(ld_r, ei);
+            }
+            if (OP == RWKV6 && KAPPA_HERE)
+                ru[j] = buf_raw1<float>(u_r, ei);
         }
-        mu[j] = buf_ld_in<float>(u_r, ei);
     }
     // GDN: the head's scalar log-decays (wave-uniform)
     float gprev = 0.f, gnew = 0.f;
@@ -386,42 +428,59 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
     // This tile's shard of the n logged value-side factors.
     const rsrc_t b_r = make_rsrc(static_cast<const char *>(a.blog) + (long)sh * M * DV * BS,
                                  MODE == EAGER ? 0 : n * DV * BS);
-    float4 bst[SB];
+    u32x4 bst[SB];
 #pragma unroll
     for (int s = 0; s < SB; ++s) {
         const int idx = tid + s * NT;
         const int m = idx / (T / 4), j4 = idx % (T / 4);
-        const unsigned e = (MODE != EAGER && idx < n * (T / 4)) ? (unsigned)(m * DV + tile * T + 4 * j4) : kSkipElem;
-        if (DELTA)
-            bst[s] = buf_ld4_in<float>(b_r, e);
-        else
-            bst[s] = buf_ld4_in<TIn>(b_r, e);
+        bst[s] = u32x4{(unsigned)tid, 0u, 0u, 0u}; // placeholder, stored to the junk slot
+        if (MODE != EAGER && s * NT + wave * 64 < n * (T / 4)) { // the wave holds live slots
+            const unsigned e = idx < n * (T / 4) ? (unsigned)(m * DV + tile * T + 4 * j4) : kSkipElem;
+            if (DELTA)
+                bst[s] = buf_raw4<float>(b_r, e);
+            else
+                bst[s] = buf_raw4<TIn>(b_r, e);
+        }
     }
     // ReplayPrep's coefficients (two-stage path)
-    float cst = 0.f;
-    if (STAGED) {
+    unsigned cst = (unsigned)tid; // placeholder for lanes past 2n+1
+    if (STAGED && wave * 64 < 2 * n + 1) {
         const rsrc_t c_r = make_rsrc(a.coef + (long)sh * a.cstride, a.cstride * 4);
         const int ci = tid < n ? tid : tid < 2 * n ? M + tid - n : 2 * M;
-        cst = buf_ldf(c_r, tid < 2 * n + 1 ? (unsigned)ci * 4u : kSkip);
+        cst = __builtin_amdgcn_raw_buffer_load_b32(c_r, tid < 2 * n + 1 ? (unsigned)ci * 4u : kSkip, 0, 0);
     }
     // log entries for this wave's share of the replay coefficients (FUSED)
-    float ea[EW][KPL], el[EW][KPL], eg[EW];
+    unsigned ea[EW][KPL], el[EW][KPL]; // raw words
+    float eg[EW];
     const rsrc_t a_r = make_rsrc(static_cast<const TIn *>(a.alog) + (long)sh * M * DK, FUSED ? n * DK * ES : 0);
 #pragma unroll
     for (int e = 0; e < EW; ++e) {
         const int m = wave + NW * e;
-        eg[e] = (FUSED && OP == GDN && m < n) ? L[m] : 0.f;
+        eg[e] = 0.f;
 #pragma unroll
-        for (int c = 0; c < KPL; ++c) {
-            const int i = lane + 64 * c;
-            const unsigned ei = (FUSED && m < n && i < DK) ? (unsigned)(m * DK + i) : kSkipElem;
-            ea[e][c] = buf_ld_in<TIn>(a_r, ei);
-            el[e][c] = OP != GDN ? buf_ld_in<float>(L_r, ei) : 0.f;
+        for (int c = 0; c < KPL; ++c)
+        {
+            ea[e][c] = (unsigned)tid; // placeholders: entries m >= n are never used
+            el[e][c] = (unsigned)tid;
+        }
+        if (FUSED && m < n) { // wave-uniform
+            if (OP == GDN)
+                eg[e] = L[m];
+#pragma unroll
+            for (int c = 0; c < KPL; ++c) {
+                const int i = lane + 64 * c;
+                const unsigned ei = i < DK ? (unsigned)(m * DK + i) : kSkipElem;
+                ea[e][c] = buf_raw1<TIn>(a_r, ei);
+                if (OP != GDN)
+                    el[e][c] = buf_raw1<float>(L_r, ei);
+            }
         }
     }
-    // v and beta for the lanes that finalise (lanes < LPR)
+    // v and beta for the lanes that finalise (lanes < LPR, all in wave 0)
     const rsrc_t v_r = make_rsrc(static_cast<const TIn *>(a.v) + (long)sh * DV, READS ? DV * ES : 0);
-    const float4 vv = buf_ld4_in<TIn>(v_r, (READS && tid < LPR) ? (unsigned)col : kSkipElem);
+    u32x4 vraw = u32x4{(unsigned)tid, 0u, 0u, 0u}; // placeholder outside wave 0
+    if (READS && wave == 0)
+        vraw = buf_raw4<TIn>(v_r, tid < LPR ? (unsigned)col : kSkipElem);
     const float bet = (READS && DELTA) ? a.beta[sh] : 0.f;
 
     // ------------------------------------------------ 1. the tile's base rows --
@@ -433,6 +492,16 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
         x[p] = buf_ld4(tile_r, xoff, p * RPP * DV * 4);
 
     // ---------------------------------------- 2. publish the small data in LDS --
+    float mq[RW], mk[RW], mprev[RW], mcur[RW], mell[RW], mu[RW];
+#pragma unroll
+    for (int j = 0; j < RW; ++j) {
+        mq[j] = cvt1<TIn>(rq_[j], tid + j * NT);
+        mk[j] = cvt1<TIn>(rk_[j], tid + j * NT);
+        mprev[j] = n > 0 ? __uint_as_float(rprev[j]) : 0.f; // Lam_{-1} = 0
+        mcur[j] = __uint_as_float(rcur[j]);
+        mell[j] = __uint_as_float(rell[j]);
+        mu[j] = __uint_as_float(ru[j]);
+    }
 #pragma unroll
     for (int j = 0; j < RW; ++j) {
         const int i = tid + j * NT;
@@ -472,7 +541,10 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
             if (MODE == FMERGE)
                 (ok ? F + n * DK + i : junk)[0] = mk[j]; // this step's entry folds with k
             if (MODE == FAPPEND && tile == 0 && ok) {   // key-side append of entry n
-                static_cast<TIn *>(a.alog)[((long)sh * M + n) * DK + i] = to_in<TIn>(mk[j]);
+                // a_n = k as whole 32-bit words: for bf16 the even lane stores
+                // the raw word holding k[i] and k[i+1]
+                if (sizeof(TIn) == 4 || (i & 1) == 0)
+                    *reinterpret_cast<unsigned *>(static_cast<TIn *>(a.alog) + ((long)sh * M + n) * DK + i) = rk_[j];
                 if (OP != GDN)
                     L[(long)n * DK + i] = lnew;
             }
@@ -488,11 +560,11 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
             const int idx = tid + s * NT;
             const int m = idx / (T / 4), j4 = idx % (T / 4);
             float *dst = idx < n * (T / 4) ? Bt + m * T + 4 * j4 : junk;
-            *reinterpret_cast<float4 *>(dst) = bst[s];
+            *reinterpret_cast<float4 *>(dst) = DELTA ? cvt4<float>(bst[s]) : cvt4<TIn>(bst[s]);
         }
     }
     if (STAGED)
-        (tid < 2 * n + 1 ? cf + tid : junk)[0] = cst;
+        (tid < 2 * n + 1 ? cf + tid : junk)[0] = __uint_as_float(cst);
     __syncthreads();
 
     // ------------- 3. FUSED: this wave's replay coefficients (and fold rows)
@@ -507,8 +579,8 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
                     for (int c = 0; c < KPL; ++c) {
                         const int i = lane + 64 * c;
                         const unsigned ei = (m < n && i < DK) ? (unsigned)(m * DK + i) : kSkipElem;
-                        ea[e][c] = buf_ld_in<TIn>(a_r, ei);
-                        el[e][c] = OP != GDN ? buf_ld_in<float>(L_r, ei) : 0.f;
+                        ea[e][c] = buf_raw1<TIn>(a_r, ei);
+                        el[e][c] = OP != GDN ? buf_raw1<float>(L_r, ei) : 0u;
                     }
                 }
             }
@@ -525,15 +597,14 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
                     const int i = lane + 64 * c;
                     if (i >= DK)
                         continue;
+                    const float am = cvt1<TIn>(ea[e][c], i), lm = __uint_as_float(el[e][c]);
                     // e^{Lam_x,i - Lam_m,i} a_m,i (GDN: scalar factor applied after the sum)
-                    const float f = OP == GDN ? ea[e][c] : expf(Lx[i] - el[e][c]) * ea[e][c];
+                    const float f = OP == GDN ? am : expf(Lx[i] - lm) * am;
                     sq = fmaf(f, Qr[i], sq);
                     if (DELTA)
                         sk = fmaf(f, Kr[i], sk);
                     if (MODE == FMERGE) // fold row: e^{Lam' - Lam_m} a_m
-                        F[m * DK + i] = OP == GDN ? g * ea[e][c]
-                                      : OP == KDA ? f
-                                                  : expf(Lf[i] - el[e][c]) * ea[e][c];
+                        F[m * DK + i] = OP == GDN ? g * am : OP == KDA ? f : expf(Lf[i] - lm) * am;
                 }
                 sq = wave_sum_from<1>(sq);
                 if (DELTA)
@@ -637,6 +708,7 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
                 }
             }
         }
+        const float4 vv = cvt4<TIn>(vraw);
         const float vs[4] = {vv.x, vv.y, vv.z, vv.w};
         float bt[4], ov[4];
 #pragma unroll
