@@ -184,6 +184,39 @@ def run_deltalog(w, inp, sts, K: int, W: int, instrument: bool, path: str = "fus
     return wall, launches, prep
 
 
+def run_graph(w, inp, sts, K: int):
+    """The same steps replayed from a HIP graph: one merge cycle of every
+    state (R*M launches, each state's steps interleaved as in the timed loop)
+    captured once, replayed K/(R*M) times.  Returns wall ms per step."""
+    import torch
+    import recurrent_state_update_amd as rsu
+    R = len(sts)
+    pool = inp["q"].shape[0]
+    ptrs = [_ptrs(inp, s) for s in range(pool)]
+    o = torch.empty(w.B, w.H, w.dv, device="cuda")
+    for st in sts:  # start every state at an empty log
+        st.merge()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sp = torch.cuda.current_stream().cuda_stream
+        for i in range(R * w.M):
+            q, k, v, beta, ld = ptrs[i % pool]
+            if rsu._lib.dl_decode_step(sts[i % R]._h, q, k, v, beta, ld, o.data_ptr(), sp) != 0:
+                raise RuntimeError("dl_decode_step failed under capture")
+    reps = max(1, K // (R * w.M))
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / (reps * R * w.M)
+
+
 def run_eager(w, inp, bases, u_dev, K: int, W: int, instrument: bool):
     import torch
     import recurrent_state_update_amd as rsu
@@ -314,6 +347,8 @@ def bench_workload(w, K, W, R, pool, with_eager=True, with_staged=True):
     if R > 1:
         one, _, _ = run_deltalog(w, inp, sts[:1], K, W, instrument=False)
         res["single_state_value"] = round(w.BH * K / (one * 1e-3), 1)
+    gms = run_graph(w, inp, sts, K)
+    res["graph_replay"] = dict(value=round(w.BH / (gms * 1e-3), 1), ms_per_step=round(gms, 5))
     if with_staged:
         sw, _, _ = run_deltalog(w, inp, sts, K, W, instrument=False, path="staged")
         _, sl, sp = run_deltalog(w, inp, sts, K, W, instrument=True, path="staged")
@@ -434,6 +469,7 @@ def main():
         "cpu_baseline": cpu,
         "modelled_step_GBs": res["modelled_step_GBs"],
         "single_state_value": res.get("single_state_value"),
+        "graph_replay": res.get("graph_replay"),
         "two_stage": res.get("two_stage"),
         "eager_same_gpu": res.get("eager_same_gpu"),
         "other_workloads": others or None,

@@ -134,6 +134,19 @@ dl_status dl_eager_step(dl_op op, int B, int H, int d_k, int d_v, dl_dtype in_dt
                         const void *q, const void *k, const void *v, const float *beta,
                         const float *log_decay, const float *u, float *o, void *stream);
 
+/* The merge interval M in [1, 32] that minimises the modelled HBM bytes per
+ * decode step of dl_decode_step for this shape ("Traffic model" section of the
+ * gist.science summary: appends of O(d_k + d_v) factors replace full writes,
+ * one dense write every M steps, and a log replay that grows with M).  Per
+ * slot-head, averaged over an M-cycle (mean log length (M-1)/2):
+ *   bytes(M) = P (1 + 1/M)                  base read every step, write per merge
+ *            + (M-1)/2 (E_key * tiles + E_val)   replay of the logged entries
+ *            + (M-1)/M E_app                 appended entry (none on the merge)
+ * with P = 4 d_k d_v, E_key = a_j + Lambda_j bytes (re-read by each of the
+ * d_v/min(d_v, 64) value tiles), E_val = b_j bytes, E_app = E_key + E_val.
+ * Returns 0 for invalid arguments. */
+int dl_suggest_merge_interval(int B, int H, int d_k, int d_v, dl_op op, dl_dtype in_dtype);
+
 /* Static description of a status code. */
 const char *dl_status_string(dl_status st);
 

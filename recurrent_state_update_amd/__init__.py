@@ -29,10 +29,10 @@ STATUS = {0: "DL_OK", 1: "DL_E_INVALID", 2: "DL_E_SHAPE", 3: "DL_E_ALIGN", 4: "D
           5: "DL_E_STATE"}
 EXPORTS = ("dl_workspace_bytes", "dl_state_create", "dl_decode_step", "dl_replay_prep",
            "dl_append_decode", "dl_merge", "dl_state_reset", "dl_log_len", "dl_set_log_len",
-           "dl_state_destroy", "dl_eager_step", "dl_status_string")
+           "dl_state_destroy", "dl_eager_step", "dl_status_string", "dl_suggest_merge_interval")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built; run `python -m recurrent_state_update_amd._build` "
+    raise ImportError(f"{LIB_PATH} is not built; run `python recurrent_state_update_amd/_build.py` "
                       "(or __graft_entry__.build())")
 
 _lib = ctypes.CDLL(LIB_PATH)
@@ -50,6 +50,7 @@ _SIG = {
     "dl_state_destroy": ([_p], _i),
     "dl_eager_step": ([_i] * 6 + [_p] * 9, _i),
     "dl_status_string": ([_i], ctypes.c_char_p),
+    "dl_suggest_merge_interval": ([_i] * 6, _i),
 }
 for _name, (_args, _res) in _SIG.items():
     _f = getattr(_lib, _name)
@@ -139,6 +140,10 @@ def dl_state_destroy(s):
 def dl_eager_step(op, B, H, d_k, d_v, in_dtype, S, q, k, v, beta, log_decay, u, o, stream=None):
     return _lib.dl_eager_step(op, B, H, d_k, d_v, in_dtype, _ptr(S), _ptr(q), _ptr(k), _ptr(v),
                               _ptr(beta), _ptr(log_decay), _ptr(u), _ptr(o), _stream(stream))
+
+
+def dl_suggest_merge_interval(B, H, d_k, d_v, op, in_dtype) -> int:
+    return int(_lib.dl_suggest_merge_interval(B, H, d_k, d_v, op, in_dtype))
 
 
 def dl_status_string(st) -> str:

@@ -1,7 +1,10 @@
 """Build step of libdeltalog: compiles the HIP sources for gfx950 with hipcc
 and links ``libdeltalog.so`` next to this file.
 
-    python -m recurrent_state_update_amd._build
+    python recurrent_state_update_amd/_build.py
+
+(run as a file, not as a module of the package: importing the package loads
+the built library, which may be the stale one this step replaces).
 
 Extra ``-D`` defines (for example a different value-tile width) can be passed
 through ``build(defines=[...], out=...)`` to produce a variant library.

@@ -314,6 +314,29 @@ dl_status dl_eager_step(dl_op op, int B, int H, int d_k, int d_v, dl_dtype in_dt
     return DL_OK;
 }
 
+int dl_suggest_merge_interval(int B, int H, int d_k, int d_v, dl_op op, dl_dtype in_dtype)
+{
+    if (check_shape(B, H, d_k, d_v, 1, op, in_dtype) != DL_OK)
+        return 0;
+    const double es = in_dtype == DL_BF16 ? 2.0 : 4.0;
+    const double P = 4.0 * d_k * d_v;
+    const double lsz = op == DL_OP_GDN ? 4.0 : 4.0 * d_k;
+    const double e_key = d_k * es + lsz;
+    const double e_val = d_v * (op == DL_OP_RWKV6 ? es : 4.0);
+    const double tiles = d_v / (double)(d_v < 64 ? d_v : 64);
+    int best = 1;
+    double best_bytes = 0.0;
+    for (int M = 1; M <= 32; ++M) {
+        const double bytes = P * (1.0 + 1.0 / M) + 0.5 * (M - 1) * (e_key * tiles + e_val) +
+                             (double)(M - 1) / M * (e_key + e_val);
+        if (M == 1 || bytes < best_bytes) {
+            best = M;
+            best_bytes = bytes;
+        }
+    }
+    return best;
+}
+
 const char *dl_status_string(dl_status st)
 {
     switch (st) {

@@ -133,3 +133,27 @@ def test_binding_refuses_host_tensors():
     with pytest.raises(ValueError):
         rsu.DeltaLogState("gdn", 1, 2, 16, 16, 4, dtype=torch.float32,
                           base=torch.zeros(1, 2, 16, 16))
+
+
+def test_suggest_merge_interval():
+    """The suggested M minimises the documented per-step byte model: check it
+    against the model's stationary point sqrt(2 (P - E_app) / (E_key*tiles +
+    E_val)), within the rounding to an integer, and its basic trends."""
+    import math
+    s = rsu.dl_suggest_merge_interval
+    for op in (GDN, KDA, RWKV6):
+        for d in (16, 32, 64, 128):
+            for dt in (F32, BF16):
+                M = s(64, 32, d, d, op, dt)
+                es = 2 if dt == BF16 else 4
+                lsz = 4 if op == GDN else 4 * d
+                e_key, e_val = d * es + lsz, d * (es if op == RWKV6 else 4)
+                tiles = d // min(d, 64)
+                P = 4 * d * d
+                m_star = math.sqrt(2 * (P - e_key - e_val) / (e_key * tiles + e_val))
+                assert 1 <= M <= 32
+                assert abs(M - min(max(m_star, 1), 32)) <= 1.0, (op, d, dt, M, m_star)
+    # a larger state defers merges longer; heavier per-key metadata merges sooner
+    assert s(64, 32, 128, 128, GDN, BF16) > s(64, 32, 32, 32, GDN, BF16)
+    assert s(64, 32, 128, 128, GDN, BF16) >= s(64, 32, 128, 128, KDA, BF16)
+    assert s(0, 1, 16, 16, GDN, F32) == 0 and s(1, 1, 24, 16, GDN, F32) == 0
