@@ -116,7 +116,8 @@ dl_status dl_merge(dl_state *s, void *stream);
  * updates.  For restarting a handle over a freshly written base. */
 dl_status dl_state_reset(dl_state *s);
 
-/* Number of pending log entries, 0..M-1 (-1 for a NULL handle). */
+/* Number of pending log entries, 0..M-1 (-1 for a NULL handle or a handle
+ * with per-slot logs: use dl_slot_log_len). */
 int dl_log_len(const dl_state *s);
 
 /* Set the number of pending entries to n (0..M-1) after the caller restored
@@ -146,6 +147,36 @@ dl_status dl_eager_step(dl_op op, int B, int H, int d_k, int d_v, dl_dtype in_dt
  * d_v/min(d_v, 64) value tiles), E_val = b_j bytes, E_app = E_key + E_val.
  * Returns 0 for invalid arguments. */
 int dl_suggest_merge_interval(int B, int H, int d_k, int d_v, dl_op op, dl_dtype in_dtype);
+
+/* ------------------------------------------------------------------------
+ * Per-slot logs, for continuous batching.  The pages apply the schedule per
+ * (slot, head) ("Kernel implementation": ReplayPrep runs per slot-head); with
+ * per-slot logs each slot (a request) keeps its own log length, so requests
+ * admitted at different steps merge at different steps.  Every decode step
+ * still covers all B slots in one launch, in which each slot appends or, when
+ * its log is full, merges.  None of these calls allocates, and all are
+ * capturable into HIP graphs.
+ * ------------------------------------------------------------------------ */
+
+/* Switch a handle to per-slot logs.  Needs an empty log (a fresh handle, or
+ * after dl_merge); every slot starts empty.  Afterwards dl_decode_step and
+ * dl_merge act per slot; dl_replay_prep, dl_append_decode, dl_set_log_len and
+ * dl_state_reset return DL_E_STATE. */
+dl_status dl_state_enable_slots(dl_state *s, void *stream);
+
+/* Admit a new request into `slot`: drop the slot's pending log without
+ * folding it.  The caller writes the request's initial state into the slot's
+ * rows of `base` ([slot, 0..H)) before the next step (stream-ordered). */
+dl_status dl_slot_admit(dl_state *s, int slot, void *stream);
+
+/* Fold the pending entries of one slot into its rows of `base` (which then
+ * hold that slot's logical state) and empty its log.  No-op when the slot's
+ * log is empty.  Use before reading a finished request's state. */
+dl_status dl_slot_merge(dl_state *s, int slot, void *stream);
+
+/* Pending entries of one slot (the shared count on a lockstep handle), -1 for
+ * a bad handle or slot. */
+int dl_slot_log_len(const dl_state *s, int slot);
 
 /* Static description of a status code. */
 const char *dl_status_string(dl_status st);

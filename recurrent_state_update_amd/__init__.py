@@ -29,7 +29,8 @@ STATUS = {0: "DL_OK", 1: "DL_E_INVALID", 2: "DL_E_SHAPE", 3: "DL_E_ALIGN", 4: "D
           5: "DL_E_STATE"}
 EXPORTS = ("dl_workspace_bytes", "dl_state_create", "dl_decode_step", "dl_replay_prep",
            "dl_append_decode", "dl_merge", "dl_state_reset", "dl_log_len", "dl_set_log_len",
-           "dl_state_destroy", "dl_eager_step", "dl_status_string", "dl_suggest_merge_interval")
+           "dl_state_destroy", "dl_eager_step", "dl_status_string", "dl_suggest_merge_interval",
+           "dl_state_enable_slots", "dl_slot_admit", "dl_slot_merge", "dl_slot_log_len")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run `python recurrent_state_update_amd/_build.py` "
@@ -51,6 +52,10 @@ _SIG = {
     "dl_eager_step": ([_i] * 6 + [_p] * 9, _i),
     "dl_status_string": ([_i], ctypes.c_char_p),
     "dl_suggest_merge_interval": ([_i] * 6, _i),
+    "dl_state_enable_slots": ([_p, _p], _i),
+    "dl_slot_admit": ([_p, _i, _p], _i),
+    "dl_slot_merge": ([_p, _i, _p], _i),
+    "dl_slot_log_len": ([_p, _i], _i),
 }
 for _name, (_args, _res) in _SIG.items():
     _f = getattr(_lib, _name)
@@ -146,6 +151,22 @@ def dl_suggest_merge_interval(B, H, d_k, d_v, op, in_dtype) -> int:
     return int(_lib.dl_suggest_merge_interval(B, H, d_k, d_v, op, in_dtype))
 
 
+def dl_state_enable_slots(s, stream=None):
+    return _lib.dl_state_enable_slots(s, _stream(stream))
+
+
+def dl_slot_admit(s, slot, stream=None):
+    return _lib.dl_slot_admit(s, slot, _stream(stream))
+
+
+def dl_slot_merge(s, slot, stream=None):
+    return _lib.dl_slot_merge(s, slot, _stream(stream))
+
+
+def dl_slot_log_len(s, slot) -> int:
+    return _lib.dl_slot_log_len(s, slot)
+
+
 def dl_status_string(st) -> str:
     return _lib.dl_status_string(st).decode()
 
@@ -227,6 +248,19 @@ class DeltaLogState:
     @property
     def log_len(self) -> int:
         return dl_log_len(self._h)
+
+    # per-slot logs (continuous batching)
+    def enable_slots(self, stream=None):
+        _check(dl_state_enable_slots(self._h, stream), "dl_state_enable_slots")
+
+    def admit(self, slot: int, stream=None):
+        _check(dl_slot_admit(self._h, slot, stream), "dl_slot_admit")
+
+    def merge_slot(self, slot: int, stream=None):
+        _check(dl_slot_merge(self._h, slot, stream), "dl_slot_merge")
+
+    def slot_log_len(self, slot: int) -> int:
+        return dl_slot_log_len(self._h, slot)
 
     def set_log_len(self, n: int):
         _check(dl_set_log_len(self._h, n), "dl_set_log_len")

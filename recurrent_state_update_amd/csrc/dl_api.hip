@@ -25,17 +25,23 @@ struct dl_state {
     char *ws;
     const float *u;
     dl::Layout lay;
-    int n;        // pending log entries
+    int n;        // pending log entries (lockstep schedule)
     bool prepped; // ReplayPrep ran for the step in progress
+    // per-slot schedule (continuous batching): slot b holds (tm - t0[b]) mod M
+    // entries; t0 is mirrored here and in the workspace
+    bool per_slot;
+    int tm;       // steps taken, mod M
+    int *t0;      // host mirror [B]
 };
 
 namespace dl {
 
 static size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-Layout workspace_layout(long BH, int dk, int dv, int M, int op, int dtype)
+Layout workspace_layout(long B, long H, int dk, int dv, int M, int op, int dtype)
 {
     const size_t es = dtype == BF16 ? 2 : 4; // input element size
+    const long BH = B * H;
     Layout l{};
     l.cstride = 2 * M + 2;
     l.a_off = 0;
@@ -44,8 +50,27 @@ Layout workspace_layout(long BH, int dk, int dv, int M, int op, int dtype)
     l.L_off = round_up(l.b_off + (size_t)BH * M * dv * bsz, 256);
     const size_t lsz = op == GDN ? (size_t)BH * M * 4 : (size_t)BH * M * dk * 4;
     l.c_off = round_up(l.L_off + lsz, 256);
-    l.total = round_up(l.c_off + (size_t)BH * l.cstride * 4, 256);
+    l.t_off = round_up(l.c_off + (size_t)BH * l.cstride * 4, 256);
+    l.total = round_up(l.t_off + (size_t)B * 4, 256);
     return l;
+}
+
+// Set the phase of one slot (or of all when slot < 0).  A kernel rather than
+// a memset so that calls stay capturable into HIP graphs.
+__global__ void slot_phase_kernel(int *t0, int B, int slot, int value)
+{
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b < B && (slot < 0 || b == slot))
+        t0[b] = value;
+}
+
+hipError_t launch_slot_phase(int *t0, int B, int slot, int value, hipStream_t st)
+{
+    const int blocks = slot >= 0 ? 1 : (B + 255) / 256;
+    const int first = slot >= 0 ? slot : 0;
+    hipLaunchKernelGGL(slot_phase_kernel, dim3(blocks), dim3(slot >= 0 ? 1 : 256), 0, st,
+                       t0 + first, slot >= 0 ? 1 : B, slot >= 0 ? 0 : -1, value);
+    return hipGetLastError();
 }
 
 } // namespace dl
@@ -98,8 +123,13 @@ dl::StepArgs make_args(const dl_state *s)
     a.Llog = reinterpret_cast<float *>(s->ws + s->lay.L_off);
     a.coef = reinterpret_cast<float *>(s->ws + s->lay.c_off);
     a.cstride = s->lay.cstride;
+    a.tm = s->tm;
+    a.t0 = reinterpret_cast<const int *>(s->ws + s->lay.t_off);
+    a.slot = -1;
     return a;
 }
+
+int *slot_phases(const dl_state *s) { return reinterpret_cast<int *>(s->ws + s->lay.t_off); }
 
 hipError_t launch_prep(int op, int dtype, int dk, const dl::StepArgs &a, hipStream_t st)
 {
@@ -128,7 +158,7 @@ size_t dl_workspace_bytes(int B, int H, int d_k, int d_v, int M, dl_op op, dl_dt
 {
     if (check_shape(B, H, d_k, d_v, M, op, in_dtype) != DL_OK)
         return 0;
-    return dl::workspace_layout((long)B * H, d_k, d_v, M, op, in_dtype).total;
+    return dl::workspace_layout(B, H, d_k, d_v, M, op, in_dtype).total;
 }
 
 dl_status dl_state_create(int B, int H, int d_k, int d_v, int M, dl_op op, dl_dtype in_dtype,
@@ -145,8 +175,12 @@ dl_status dl_state_create(int B, int H, int d_k, int d_v, int M, dl_op op, dl_dt
     if (!aligned(base, 16) || !aligned(workspace, 256) || (u && !aligned(u, 4)))
         return DL_E_ALIGN;
     dl_state *s = new (std::nothrow) dl_state;
-    if (!s)
+    int *t0 = new (std::nothrow) int[B];
+    if (!s || !t0) {
+        delete s;
+        delete[] t0;
         return DL_E_INVALID;
+    }
     s->B = B;
     s->H = H;
     s->dk = d_k;
@@ -157,9 +191,14 @@ dl_status dl_state_create(int B, int H, int d_k, int d_v, int M, dl_op op, dl_dt
     s->base = base;
     s->ws = static_cast<char *>(workspace);
     s->u = op == DL_OP_RWKV6 ? u : nullptr;
-    s->lay = dl::workspace_layout((long)B * H, d_k, d_v, M, op, in_dtype);
+    s->lay = dl::workspace_layout(B, H, d_k, d_v, M, op, in_dtype);
     s->n = 0;
     s->prepped = false;
+    s->per_slot = false;
+    s->tm = 0;
+    s->t0 = t0;
+    for (int b = 0; b < B; ++b)
+        t0[b] = 0;
     *out = s;
     return DL_OK;
 }
@@ -169,7 +208,7 @@ dl_status dl_replay_prep(dl_state *s, const void *q, const void *k, const float 
 {
     if (!s || !q || !k || !log_decay)
         return DL_E_INVALID;
-    if (s->prepped)
+    if (s->prepped || s->per_slot)
         return DL_E_STATE;
     const size_t es = s->dtype == DL_BF16 ? 2 : 4;
     if (!aligned(q, es) || !aligned(k, es) || !aligned(log_decay, 4))
@@ -189,7 +228,7 @@ dl_status dl_append_decode(dl_state *s, const void *q, const void *k, const void
 {
     if (!s)
         return DL_E_INVALID;
-    if (!s->prepped)
+    if (!s->prepped || s->per_slot)
         return DL_E_STATE;
     // this stage does not read the log-decay: ReplayPrep stored Lam'
     const dl_status st = check_step_ptrs(s->op, s->dtype, q, k, v, beta, nullptr, o, false);
@@ -227,6 +266,13 @@ dl_status dl_decode_step(dl_state *s, const void *q, const void *k, const void *
     a.beta = beta;
     a.ld = log_decay;
     a.o = o;
+    if (s->per_slot) { // every slot appends or merges by its own phase
+        if (launch_step(s->op, s->dtype, s->dk, s->dv, dl::SSTEP, a, static_cast<hipStream_t>(stream)) !=
+            hipSuccess)
+            return DL_E_HIP;
+        s->tm = (s->tm + 1) % s->M;
+        return DL_OK;
+    }
     const bool merge = s->n + 1 == s->M;
     if (launch_step(s->op, s->dtype, s->dk, s->dv, merge ? dl::FMERGE : dl::FAPPEND, a,
                     static_cast<hipStream_t>(stream)) !=
@@ -242,6 +288,16 @@ dl_status dl_merge(dl_state *s, void *stream)
         return DL_E_INVALID;
     if (s->prepped)
         return DL_E_STATE;
+    if (s->per_slot) {
+        dl::StepArgs a = make_args(s);
+        const hipStream_t st = static_cast<hipStream_t>(stream);
+        if (launch_step(s->op, s->dtype, s->dk, s->dv, dl::SFOLD, a, st) != hipSuccess ||
+            dl::launch_slot_phase(slot_phases(s), s->B, -1, s->tm, st) != hipSuccess)
+            return DL_E_HIP;
+        for (int b = 0; b < s->B; ++b)
+            s->t0[b] = s->tm;
+        return DL_OK;
+    }
     if (s->n == 0)
         return DL_OK;
     dl::StepArgs a = make_args(s);
@@ -256,12 +312,14 @@ dl_status dl_state_reset(dl_state *s)
 {
     if (!s)
         return DL_E_INVALID;
+    if (s->per_slot)
+        return DL_E_STATE;
     s->n = 0;
     s->prepped = false;
     return DL_OK;
 }
 
-int dl_log_len(const dl_state *s) { return s ? s->n : -1; }
+int dl_log_len(const dl_state *s) { return (s && !s->per_slot) ? s->n : -1; }
 
 dl_status dl_set_log_len(dl_state *s, int n)
 {
@@ -269,7 +327,7 @@ dl_status dl_set_log_len(dl_state *s, int n)
         return DL_E_INVALID;
     if (n < 0 || n >= s->M)
         return DL_E_INVALID;
-    if (s->prepped)
+    if (s->prepped || s->per_slot)
         return DL_E_STATE;
     s->n = n;
     return DL_OK;
@@ -277,8 +335,65 @@ dl_status dl_set_log_len(dl_state *s, int n)
 
 dl_status dl_state_destroy(dl_state *s)
 {
+    if (s)
+        delete[] s->t0;
     delete s;
     return DL_OK;
+}
+
+dl_status dl_state_enable_slots(dl_state *s, void *stream)
+{
+    if (!s)
+        return DL_E_INVALID;
+    if (s->prepped || s->n != 0 || s->per_slot)
+        return DL_E_STATE;
+    if (dl::launch_slot_phase(slot_phases(s), s->B, -1, 0, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return DL_E_HIP;
+    s->per_slot = true;
+    s->tm = 0;
+    for (int b = 0; b < s->B; ++b)
+        s->t0[b] = 0;
+    return DL_OK;
+}
+
+dl_status dl_slot_admit(dl_state *s, int slot, void *stream)
+{
+    if (!s || slot < 0 || slot >= s->B)
+        return DL_E_INVALID;
+    if (!s->per_slot)
+        return DL_E_STATE;
+    if (dl::launch_slot_phase(slot_phases(s), s->B, slot, s->tm, static_cast<hipStream_t>(stream)) !=
+        hipSuccess)
+        return DL_E_HIP;
+    s->t0[slot] = s->tm;
+    return DL_OK;
+}
+
+dl_status dl_slot_merge(dl_state *s, int slot, void *stream)
+{
+    if (!s || slot < 0 || slot >= s->B)
+        return DL_E_INVALID;
+    if (!s->per_slot)
+        return DL_E_STATE;
+    if (dl_slot_log_len(s, slot) == 0)
+        return DL_OK;
+    dl::StepArgs a = make_args(s);
+    a.slot = slot;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (launch_step(s->op, s->dtype, s->dk, s->dv, dl::SFOLD, a, st) != hipSuccess ||
+        dl::launch_slot_phase(slot_phases(s), s->B, slot, s->tm, st) != hipSuccess)
+        return DL_E_HIP;
+    s->t0[slot] = s->tm;
+    return DL_OK;
+}
+
+int dl_slot_log_len(const dl_state *s, int slot)
+{
+    if (!s || slot < 0 || slot >= s->B)
+        return -1;
+    if (!s->per_slot)
+        return s->n;
+    return (s->tm - s->t0[slot] + s->M) % s->M;
 }
 
 dl_status dl_eager_step(dl_op op, int B, int H, int d_k, int d_v, dl_dtype in_dtype, float *S,

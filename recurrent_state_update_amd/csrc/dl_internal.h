@@ -18,7 +18,9 @@ enum Mode : int {
     EAGER = 2,   // eager baseline: decay, delta rule, rank-1 update, write state
     FOLD = 3,    // standalone merge: fold the n pending entries, write S-bar
     FAPPEND = 4, // one-launch append phase (replay coefficients computed in place)
-    FMERGE = 5   // one-launch merge phase
+    FMERGE = 5,  // one-launch merge phase
+    SSTEP = 6,   // one-launch step with per-slot logs: each slot appends or merges
+    SFOLD = 7    // standalone merge with per-slot logs (one slot or all)
 };
 
 // Byte offsets of the log and coefficient arrays inside the workspace.
@@ -28,11 +30,12 @@ struct Layout {
     size_t b_off;   // b-log      [B*H, M, d_v]  fp32 (delta rule) / input dtype (RWKV6)
     size_t L_off;   // Lambda-log [B*H, M] (GDN) or [B*H, M, d_k] fp32
     size_t c_off;   // coef       [B*H, cstride] fp32: c^q_0..M-1, c^k_0..M-1, kappa
+    size_t t_off;   // slot phase [B] int32 (per-slot schedule)
     size_t total;
     int cstride;
 };
 
-Layout workspace_layout(long BH, int dk, int dv, int M, int op, int dtype);
+Layout workspace_layout(long B, long H, int dk, int dv, int M, int op, int dtype);
 
 // Everything a launch needs, passed by value as the kernel argument.
 struct StepArgs {
@@ -53,6 +56,10 @@ struct StepArgs {
     float *Llog;
     float *coef;
     int cstride;
+    // per-slot schedule: slot b's log length is (tm - t0[b]) mod M
+    int tm;          // the handle's step counter mod M
+    const int *t0;   // [B] step (mod M) at which each slot's log was last emptied
+    int slot;        // SFOLD: the one slot to fold, or -1 for all
 };
 
 // Kernel launchers, one set per operator (dl_gdn.hip, dl_kda.hip, dl_rwkv6.hip).
@@ -61,6 +68,7 @@ struct StepArgs {
 hipError_t launch_prep_gdn(int dtype, int dk, const StepArgs &a, hipStream_t st);
 hipError_t launch_prep_kda(int dtype, int dk, const StepArgs &a, hipStream_t st);
 hipError_t launch_prep_rwkv6(int dtype, int dk, const StepArgs &a, hipStream_t st);
+hipError_t launch_slot_phase(int *t0, int B, int slot, int value, hipStream_t st);
 hipError_t launch_step_gdn(int dtype, int dk, int dv, int mode, const StepArgs &a, hipStream_t st);
 hipError_t launch_step_kda(int dtype, int dk, int dv, int mode, const StepArgs &a, hipStream_t st);
 hipError_t launch_step_rwkv6(int dtype, int dk, int dv, int mode, const StepArgs &a, hipStream_t st);

@@ -182,19 +182,25 @@ template <int DK, int DV> struct TileCfg {
     static_assert(P * RPP == DK && LPR <= 32 && NT % LPR == 0 && NT % 64 == 0, "tile shape");
 };
 
-__host__ __device__ constexpr bool mode_fused(int mode) { return mode == FAPPEND || mode == FMERGE; }
+__host__ __device__ constexpr bool mode_fused(int mode)
+{
+    return mode == FAPPEND || mode == FMERGE || mode == SSTEP;
+}
+__host__ __device__ constexpr bool mode_fold(int mode) { return mode == FOLD || mode == SFOLD; }
 __host__ __device__ constexpr bool mode_logged(int mode)
 {
     return mode == APPEND || mode == MERGE || mode_fused(mode);
 }
 // Rows of the staged value-side factors and of the fold table for a launch.
+// (SSTEP is sized for a merge at the longest log, the host passing n = M-1.)
 __host__ __device__ constexpr int bt_rows(int mode, int n)
 {
-    return mode == FOLD ? n : mode == EAGER ? 1 : n + 1;
+    return mode_fold(mode) ? n : mode == EAGER ? 1 : n + 1;
 }
 __host__ __device__ constexpr int fold_rows(int mode, int n)
 {
-    return (mode == MERGE || mode == FMERGE) ? n + 1 : mode == EAGER ? 1 : mode == FOLD ? n : 0;
+    return (mode == MERGE || mode == FMERGE || mode == SSTEP) ? n + 1
+         : mode == EAGER ? 1 : mode_fold(mode) ? n : 0;
 }
 constexpr int kRowTables = 8;
 // Dynamic LDS floats of the step kernel: eight per-row tables [DK], Bt
@@ -336,8 +342,14 @@ __global__ __launch_bounds__(256) void replay_prep_kernel(StepArgs a)
 //                    w, w+NW, ...) and tile 0 performs the key-side append;
 //   EAGER            the eager baseline: decay, delta rule or raw update,
 //                    rank-1 fold of this step only;
-//   FOLD             standalone merge of the n pending entries.
-// MERGE/FMERGE/EAGER/FOLD end with the fold and the single dense write.
+//   FOLD             standalone merge of the n pending entries;
+//   SSTEP, SFOLD     the one-launch step and the standalone merge for a handle
+//                    whose slots keep separate logs (continuous batching):
+//                    each workgroup derives its slot's log length from the
+//                    slot's phase, and an SSTEP workgroup merges exactly when
+//                    its slot's log is full, so one launch mixes append and
+//                    merge workgroups.
+// Merging launches end with the fold and the single dense write.
 template <int OP, typename TIn, int DK, int DV, int MODE>
 __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
 {
@@ -348,9 +360,10 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
     constexpr bool FUSED = mode_fused(MODE);
     constexpr bool STAGED = MODE == APPEND || MODE == MERGE;
     constexpr bool LOGGED = FUSED || STAGED;               // a step of the DeltaLog schedule
-    constexpr bool READS = MODE != FOLD;                   // computes o_t and b_t
-    constexpr bool MERGING = MODE == MERGE || MODE == FMERGE;
-    constexpr bool WRITES = MERGING || MODE == EAGER || MODE == FOLD;
+    constexpr bool FOLDS = mode_fold(MODE);                // standalone merge
+    constexpr bool SLOTS = MODE == SSTEP || MODE == SFOLD; // per-slot logs
+    constexpr bool READS = !FOLDS;                         // computes o_t and b_t
+    constexpr bool MAY_WRITE = !(MODE == APPEND || MODE == FAPPEND);
     constexpr bool KAPPA_HERE = FUSED || MODE == EAGER;    // q.k summed in this kernel
     constexpr int ES = sizeof(TIn);
     constexpr int BS = DELTA ? 4 : ES;                     // b-log element size
@@ -369,14 +382,22 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
     // Natural block order: consecutive workgroups (dispatched round-robin over
     // the 8 XCDs) read adjacent tiles, which streams HBM faster than giving
     // each XCD a contiguous slab of the state (measured).
-    const int sh = blockIdx.x / NTILE, tile = blockIdx.x % NTILE;
+    const int sh = (SLOTS && a.slot >= 0 ? a.slot * a.H : 0) + blockIdx.x / NTILE;
+    const int tile = blockIdx.x % NTILE;
     const int col = tile * T + 4 * c4;
-    const int M = a.M, n = a.n;
+    const int M = a.M;
+    // log length: shared by all slots, or this slot's own (wave-uniform)
+    const int n = SLOTS ? (a.tm - a.t0[sh / a.H] + M) % M : a.n;
+    if (MODE == SFOLD && n == 0)
+        return; // nothing pending for this slot (whole workgroup leaves)
+    const bool merging = MODE == MERGE || MODE == FMERGE || (MODE == SSTEP && n == M - 1);
+    const bool writes = merging || MODE == EAGER || FOLDS;
 
     float *S = a.base + (long)sh * DK * DV;
     float *L = a.Llog + (OP == GDN ? (long)sh * M : (long)sh * M * DK);
 
-    const int nb = bt_rows(MODE, n), nf = fold_rows(MODE, n);
+    const int nb = bt_rows(MODE, n);
+    const int nf = merging ? n + 1 : MODE == EAGER ? 1 : FOLDS ? n : 0;
     float *Wq = dyn;             // read weights, q side
     float *Wk = dyn + DK;        // read weights, k side
     float *Rf = dyn + 2 * DK;    // fold base factor e^{Lam_f}
@@ -432,7 +453,7 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
     float gprev = 0.f, gnew = 0.f;
     if (OP == GDN) {
         gprev = (MODE != EAGER && n > 0) ? L[n - 1] : 0.f;
-        gnew = MODE == EAGER ? a.ld[sh] : STAGED ? L[n] : MODE == FOLD ? gprev : gprev + a.ld[sh];
+        gnew = MODE == EAGER ? a.ld[sh] : STAGED ? L[n] : FOLDS ? gprev : gprev + a.ld[sh];
     }
     // This tile's shard of the n logged value-side factors.
     const rsrc_t b_r = make_rsrc(static_cast<const char *>(a.blog) + (long)sh * M * DV * BS,
@@ -521,7 +542,7 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
             lnew = lfold = gnew;
         } else {
             lnew = MODE == EAGER ? mell[j] : STAGED ? mcur[j] : mprev[j] + mell[j];
-            lfold = MODE == FOLD ? mprev[j] : lnew;
+            lfold = FOLDS ? mprev[j] : lnew;
         }
         float wq, wk = 0.f;
         if (OP == GDN) {
@@ -537,7 +558,7 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
         (ok ? Wq + i : junk)[0] = wq;
         if (DELTA)
             (ok ? Wk + i : junk)[0] = wk;
-        if (OP != GDN && WRITES) {
+        if (OP != GDN && MAY_WRITE) {
             (ok ? Rf + i : junk)[0] = expf(lfold);
             (ok ? Lf + i : junk)[0] = lfold;
         }
@@ -547,9 +568,9 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
             (ok ? Qr + i : junk)[0] = mq[j];
             (ok ? Kr + i : junk)[0] = mk[j];
             (ok ? Lx + i : junk)[0] = OP == RWKV6 ? mprev[j] : lnew;
-            if (MODE == FMERGE)
+            if (merging)
                 (ok ? F + n * DK + i : junk)[0] = mk[j]; // this step's entry folds with k
-            if (MODE == FAPPEND && tile == 0 && ok) {   // key-side append of entry n
+            if (!merging && tile == 0 && ok) {          // key-side append of entry n
                 // a_n = k as whole 32-bit words: for bf16 the even lane stores
                 // the raw word holding k[i] and k[i+1]
                 if (sizeof(TIn) == 4 || (i & 1) == 0)
@@ -561,7 +582,7 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
         if (MODE == EAGER)
             (ok ? F + i : junk)[0] = mk[j]; // the only entry folds with k
     }
-    if (OP == GDN && MODE == FAPPEND && tile == 0 && tid == 0)
+    if (OP == GDN && FUSED && !merging && tile == 0 && tid == 0)
         L[n] = gnew;
     if (MODE != EAGER) {
 #pragma unroll
@@ -612,7 +633,7 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
                     sq = fmaf(f, Qr[i], sq);
                     if (DELTA)
                         sk = fmaf(f, Kr[i], sk);
-                    if (MODE == FMERGE) // fold row: e^{Lam' - Lam_m} a_m
+                    if (merging) // fold row: e^{Lam' - Lam_m} a_m
                         F[m * DK + i] = OP == GDN ? g * am : OP == KDA ? f : expf(Lf[i] - lm) * am;
                 }
                 sq = wave_sum_from<1>(sq);
@@ -663,7 +684,7 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
     // ------- 5. fold table for MERGE / FOLD (FMERGE, EAGER built theirs above):
     //    F[m][i] = e^{Lam_f,i - Lam_m,i} a_m,i; in MERGE the entry n appended by
     //    ReplayPrep (a_n = k, Lam_n = Lam_f) gives exactly k_i.
-    if (MODE == MERGE || MODE == FOLD) {
+    if (MODE == MERGE || FOLDS) {
         const rsrc_t af_r = make_rsrc(static_cast<const TIn *>(a.alog) + (long)sh * M * DK, nf * DK * ES);
         const int total = nf * DK;
         for (int base = 0; base < total; base += 4 * NT) {
@@ -731,7 +752,7 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
             }
         }
         *reinterpret_cast<float4 *>(a.o + (long)sh * DV + col) = make_float4(ov[0], ov[1], ov[2], ov[3]);
-        if (LOGGED && !MERGING) { // value-side append of entry n (a merge empties the log)
+        if (LOGGED && !merging) { // value-side append of entry n (a merge empties the log)
             const long off = ((long)sh * M + n) * DV + col;
             if (DELTA) {
                 *reinterpret_cast<float4 *>(static_cast<float *>(a.blog) + off) =
@@ -743,12 +764,12 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
                     bl[c] = to_in<TIn>(vs[c]);
             }
         }
-        if (WRITES)
+        if (writes)
             *reinterpret_cast<float4 *>(Bt + (nb - 1) * T + 4 * c4) = make_float4(bt[0], bt[1], bt[2], bt[3]);
     }
 
     // --------------------------------------- 7. fold and write the tile once
-    if (WRITES) {
+    if (writes) { // uniform over the workgroup
         __syncthreads();
         const float gs = OP == GDN ? expf(gnew) : 1.f;
 #pragma unroll
@@ -800,8 +821,11 @@ template <int OP, typename TIn, int DK, int DV, int MODE>
 hipError_t launch_step_t(const StepArgs &a, hipStream_t st)
 {
     using C = TileCfg<DK, DV>;
-    const dim3 grid((unsigned)a.BH * C::NTILE);
-    const size_t lds = sizeof(float) * (size_t)dyn_floats(MODE, a.n, DK, C::T);
+    // per-slot launches size LDS for the longest log and may cover one slot
+    const int slot_heads = (MODE == SFOLD && a.slot >= 0) ? a.H : a.BH;
+    const int n_lds = (MODE == SSTEP || MODE == SFOLD) ? a.M - 1 : a.n;
+    const dim3 grid((unsigned)slot_heads * C::NTILE);
+    const size_t lds = sizeof(float) * (size_t)dyn_floats(MODE, n_lds, DK, C::T);
     hipLaunchKernelGGL((step_kernel<OP, TIn, DK, DV, MODE>), grid, dim3(C::NT), lds, st, a);
     return hipGetLastError();
 }
@@ -816,6 +840,8 @@ hipError_t launch_step_mode(int mode, const StepArgs &a, hipStream_t st)
     case FOLD: return launch_step_t<OP, TIn, DK, DV, FOLD>(a, st);
     case FAPPEND: return launch_step_t<OP, TIn, DK, DV, FAPPEND>(a, st);
     case FMERGE: return launch_step_t<OP, TIn, DK, DV, FMERGE>(a, st);
+    case SSTEP: return launch_step_t<OP, TIn, DK, DV, SSTEP>(a, st);
+    case SFOLD: return launch_step_t<OP, TIn, DK, DV, SFOLD>(a, st);
     }
     return hipErrorInvalidValue;
 }

@@ -157,3 +157,21 @@ def test_suggest_merge_interval():
     assert s(64, 32, 128, 128, GDN, BF16) > s(64, 32, 32, 32, GDN, BF16)
     assert s(64, 32, 128, 128, GDN, BF16) >= s(64, 32, 128, 128, KDA, BF16)
     assert s(0, 1, 16, 16, GDN, F32) == 0 and s(1, 1, 24, 16, GDN, F32) == 0
+
+
+def test_per_slot_calls_validate_before_any_launch():
+    st, h = _create(B=4, op=GDN, dt=BF16)
+    try:
+        s = 0
+        assert rsu.dl_slot_admit(h, 0, s) == STATE       # lockstep handle
+        assert rsu.dl_slot_merge(h, 1, s) == STATE
+        assert rsu.dl_slot_admit(h, 4, s) == INVALID     # slot out of range
+        assert rsu.dl_slot_admit(h, -1, s) == INVALID
+        assert rsu.dl_slot_log_len(h, 0) == 0 and rsu.dl_slot_log_len(h, 4) == -1
+        assert rsu.dl_slot_log_len(None, 0) == -1
+        assert rsu.dl_set_log_len(h, 2) == OK
+        assert rsu.dl_state_enable_slots(h, s) == STATE  # needs an empty log
+        assert rsu.dl_slot_log_len(h, 3) == 2
+        assert rsu.dl_state_enable_slots(None, s) == INVALID
+    finally:
+        rsu.dl_state_destroy(h)

@@ -297,3 +297,58 @@ def test_graph_capture_of_merge_cycles(orc, op):
         assert rel(b.base.reshape(w.BH, w.dk, w.dv).cpu().numpy(), X[0]) < FP32_TOL
     a.close()
     b.close()
+
+
+@needs_gpu
+@pytest.mark.parametrize("op", ["gdn", "kda", "rwkv6"])
+@pytest.mark.parametrize("M", [4, 8])
+def test_per_slot_logs_continuous_batching(orc, op, M):
+    """Per-slot logs: requests are admitted into slots at different steps
+    (fresh initial states written into the slot's base rows), so slots merge
+    at different steps within one launch; one slot is merged early to retire
+    its request.  Every output is checked against the eager oracle, each
+    slot's base right after its own merge, and all bases after dl_merge."""
+    import recurrent_state_update_amd as rsu
+    B, H = 5, 3
+    w = synth.Workload(18, op, B, H, 64, 128, M, 3 * M + 5, "bf16")
+    X0, u = synth.initial(w)
+    dt = in_dtype(w)
+    st = rsu.DeltaLogState(op, B, H, w.dk, w.dv, M, dtype=dt, base=dev(X0), u=dev(u))
+    st.enable_slots()
+    X = X0.reshape(B * H, w.dk, w.dv).astype(np.float64)[None].copy()
+    u_sub = None if u is None else u[np.arange(B * H) % H].astype(np.float64)
+    admissions = {1: [1], 3: [2], 5: [4, 1], M + 2: [3]}   # step -> slots admitted before it
+    retire = {M + 1: 0}                                       # step -> slot merged before it
+    worst_o = worst_S = 0.0
+    checked = 0
+    for t in range(w.steps):
+        for b in admissions.get(t, []):
+            new = synth.initial(w.with_(wid=1000 + 10 * t + b))[0][b]       # [H, dk, dv]
+            st.base[b].copy_(dev(new))
+            st.admit(b)
+            X[0, b * H:(b + 1) * H] = new.astype(np.float64)
+            assert st.slot_log_len(b) == 0
+        if t in retire:
+            b = retire[t]
+            st.merge_slot(b)
+            assert st.slot_log_len(b) == 0
+            worst_S = max(worst_S, rel(st.base[b].cpu().numpy(), X[0, b * H:(b + 1) * H]))
+        s = synth.step(w, t)
+        d = {k_: dev(v_, dt if k_ in ("q", "k", "v") else torch.float32) for k_, v_ in s.items()}
+        o = st.step(d["q"], d["k"], d["v"], d["beta"], d["ld"])
+        sub = synth.subset(s, np.arange(B * H))
+        o_ref = orc.eager_step(op, X, sub["q"], sub["k"], sub["v"], sub["beta"], sub["ld"], u_sub)
+        worst_o = max(worst_o, rel(o.reshape(B * H, w.dv).cpu().numpy(), o_ref[0]))
+        lens = [st.slot_log_len(b) for b in range(B)]
+        assert len(set(lens)) > 1 or t < 1   # slots really are out of phase
+        for b in range(B):
+            if lens[b] == 0:                 # this slot merged at this step
+                worst_S = max(worst_S, rel(st.base[b].cpu().numpy(), X[0, b * H:(b + 1) * H]))
+                checked += 1
+    st.merge()
+    assert all(st.slot_log_len(b) == 0 for b in range(B))
+    worst_S = max(worst_S, rel(st.base.reshape(B * H, w.dk, w.dv).cpu().numpy(), X[0]))
+    print(f"[{op} per-slot M={M}] worst o={worst_o:.2e} S={worst_S:.2e} merges checked {checked}")
+    assert checked >= B
+    assert worst_o < FP32_TOL and worst_S < FP32_TOL
+    st.close()
