@@ -217,6 +217,65 @@ def run_graph(w, inp, sts, K: int):
     return t0.elapsed_time(t1) / (reps * R * w.M)
 
 
+def run_per_slot(w, inp, R: int, K: int, W: int):
+    """Continuous batching: R fresh states with per-slot logs, slot b admitted
+    at step b % M, so in steady state every launch merges the B/M slots whose
+    logs are full and appends for the rest.  Returns wall ms of K launches and
+    the algorithmic bytes they move."""
+    import torch
+    import synth
+    import recurrent_state_update_amd as rsu
+    dt = inp["q"].dtype
+    X0, u = synth.initial(w)
+    u_dev = None if u is None else torch.from_numpy(u).cuda()
+    sts = [rsu.DeltaLogState(w.op, w.B, w.H, w.dk, w.dv, w.M, dtype=dt,
+                             base=torch.from_numpy(X0).cuda(), u=u_dev) for _ in range(R)]
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    pool = inp["q"].shape[0]
+    ptrs = [_ptrs(inp, s) for s in range(pool)]
+    o = torch.empty(w.B, w.H, w.dv, device="cuda")
+    L = rsu._lib
+    for st in sts:
+        st.enable_slots()
+
+    def one(i):
+        q, k, v, beta, ld = ptrs[i % pool]
+        if L.dl_decode_step(sts[i % R]._h, q, k, v, beta, ld, o.data_ptr(), sp) != 0:
+            raise RuntimeError("dl_decode_step failed on a per-slot state")
+
+    for i in range(R * w.M):            # stagger: slot b starts at step b % M
+        if i % R == 0:
+            for b in range(i // R, w.B, w.M):
+                for st in sts:
+                    st.admit(b)
+        one(i)
+    for i in range(W):
+        one(R * w.M + i)
+    ones = w.with_(B=1, H=w.H)
+    nbytes = 0
+    for i in range(K):
+        st = sts[(R * w.M + W + i) % R]
+        if i < R * w.M:                 # the schedule repeats every R*M launches
+            nbytes += sum(step_launch_bytes(ones, n, n + 1 == w.M)
+                          for n in (st.slot_log_len(b) for b in range(w.B)))
+        one(R * w.M + W + i)
+    torch.cuda.synchronize()
+    cyc = min(K, R * w.M)
+    nbytes = nbytes * K / cyc
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(K):
+        one(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = t0.elapsed_time(t1)
+    for st in sts:
+        st.close()
+    return wall, nbytes
+
+
 def run_eager(w, inp, bases, u_dev, K: int, W: int, instrument: bool):
     import torch
     import recurrent_state_update_amd as rsu
@@ -347,6 +406,10 @@ def bench_workload(w, K, W, R, pool, with_eager=True, with_staged=True):
     if R > 1:
         one, _, _ = run_deltalog(w, inp, sts[:1], K, W, instrument=False)
         res["single_state_value"] = round(w.BH * K / (one * 1e-3), 1)
+    pw, pbytes = run_per_slot(w, inp, R, K, W)
+    res["per_slot"] = dict(value=round(w.BH * K / (pw * 1e-3), 1), ms_per_step=round(pw / K, 5),
+                           achieved_GBs=round(pbytes / (pw * 1e-3) / 1e9, 1),
+                           frac=round(pbytes / (pw * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
     gms = run_graph(w, inp, sts, K)
     res["graph_replay"] = dict(value=round(w.BH / (gms * 1e-3), 1), ms_per_step=round(gms, 5))
     if with_staged:
@@ -470,6 +533,7 @@ def main():
         "modelled_step_GBs": res["modelled_step_GBs"],
         "single_state_value": res.get("single_state_value"),
         "graph_replay": res.get("graph_replay"),
+        "per_slot": res.get("per_slot"),
         "two_stage": res.get("two_stage"),
         "eager_same_gpu": res.get("eager_same_gpu"),
         "other_workloads": others or None,
