@@ -157,3 +157,59 @@ def subset(d: dict, idx: np.ndarray, lead: int = 0) -> dict:
         sel = np.take(flat, idx, axis=lead)
         out[key] = sel.reshape(a.shape[:lead] + (1, len(idx)) + a.shape[lead + 2:])
     return out
+
+
+# ------------------------------------------------------- decoder harness --
+@dataclass(frozen=True)
+class DecoderShape:
+    """A synthetic stack of L recurrent layers around the decode step."""
+    op: str
+    L: int
+    B: int
+    H: int
+    dk: int
+    dv: int
+    M: int
+    hidden: int
+    ffn: int
+    seed: int = 0
+
+    def describe(self) -> str:
+        return (f"{self.op} L={self.L} B={self.B} H={self.H} dk={self.dk} dv={self.dv} "
+                f"M={self.M} hidden={self.hidden} ffn={self.ffn}")
+
+    @property
+    def proj_split(self) -> list:
+        """Widths of the input projection's column blocks: q (r), k, v, beta
+        logits (none for RWKV6), decay logits (per head for GDN, per key else)."""
+        H = self.H
+        nb = 0 if self.op == "rwkv6" else H
+        nd = H if self.op == "gdn" else H * self.dk
+        return [H * self.dk, H * self.dk, H * self.dv, nb, nd]
+
+
+def _drng(ds: DecoderShape, stream: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(
+        np.random.SeedSequence([1000 + ds.seed, OP_IDS[ds.op], stream])))
+
+
+def decoder_layer(ds: DecoderShape, layer: int) -> dict:
+    """Random weights of one layer, float32, each N(0, 1/fan_in): W_in
+    [hidden, sum(proj_split)], W_o [H*dv, hidden], W_gu [hidden, 2*ffn] (gate
+    then up), W_dn [ffn, hidden]; RWKV6's u [H, dk] ~ N(0, 0.1) (else None);
+    and the layer's initial state [B, H, dk, dv] ~ N(0, 0.1).  Draw order as
+    listed, from stream layer+1."""
+    rng = _drng(ds, layer + 1)
+    n_in = sum(ds.proj_split)
+    out = {}
+    for name, (fi, fo) in (("W_in", (ds.hidden, n_in)), ("W_o", (ds.H * ds.dv, ds.hidden)),
+                           ("W_gu", (ds.hidden, 2 * ds.ffn)), ("W_dn", (ds.ffn, ds.hidden))):
+        out[name] = _normal(rng, (fi, fo), 0.0, 1.0 / np.sqrt(fi))
+    out["u"] = _normal(rng, (ds.H, ds.dk), 0.0, 0.1) if ds.op == "rwkv6" else None
+    out["X0"] = _normal(rng, (ds.B, ds.H, ds.dk, ds.dv), 0.0, 0.1)
+    return out
+
+
+def decoder_input(ds: DecoderShape) -> np.ndarray:
+    """The first step's hidden input [B, hidden] ~ N(0, 1), stream 0."""
+    return _normal(_drng(ds, 0), (ds.B, ds.hidden))

@@ -83,3 +83,19 @@ def test_subset_keeps_slot_heads():
     flat = d["k"].reshape(2, w.B * w.H, w.dk)
     assert sub["k"].shape == (2, 1, 4, w.dk)
     assert np.array_equal(sub["k"][:, 0], flat[:, idx])
+
+
+def test_decoder_params_are_seeded_and_scaled():
+    ds = synth.DecoderShape("kda", L=2, B=2, H=3, dk=16, dv=32, M=4, hidden=256, ffn=384)
+    a, b = synth.decoder_layer(ds, 1), synth.decoder_layer(ds, 1)
+    c = synth.decoder_layer(ds, 0)
+    for k in ("W_in", "W_o", "W_gu", "W_dn", "X0"):
+        assert np.array_equal(a[k], b[k]) and not np.array_equal(a[k], c[k])
+    assert a["W_in"].shape == (256, sum(ds.proj_split)) == (256, 3 * 16 + 3 * 16 + 3 * 32 + 3 + 3 * 16)
+    assert a["W_gu"].shape == (256, 768) and a["W_dn"].shape == (384, 256)
+    assert abs(a["W_in"].std() * np.sqrt(256) - 1) < 0.02 and abs(a["W_dn"].std() * np.sqrt(384) - 1) < 0.02
+    assert a["u"] is None and synth.decoder_layer(ds.__class__(**{**ds.__dict__, "op": "rwkv6"}), 0)["u"].shape == (3, 16)
+    assert synth.DecoderShape("gdn", 1, 1, 4, 16, 16, 2, 8, 8).proj_split == [64, 64, 64, 4, 4]
+    assert synth.DecoderShape("rwkv6", 1, 1, 4, 16, 16, 2, 8, 8).proj_split == [64, 64, 64, 0, 64]
+    x = synth.decoder_input(ds)
+    assert x.shape == (2, 256) and np.array_equal(x, synth.decoder_input(ds))
