@@ -35,8 +35,10 @@
 // once.  Loads that a lane does not need are pointed past the end of a
 // bounds-limited buffer resource: they return zero without touching memory,
 // which keeps the code branch-free (no load gets sunk behind a wait) and adds
-// no traffic.  Column sums reduce across lanes with xor-shuffles and across
-// waves through LDS.
+// no traffic.  Column sums reduce across lanes in registers (DPP row rotations
+// and the permlane swaps) and across waves through LDS.  Register use is kept
+// at or under 64 VGPRs on the hot modes where it can be, which lets eight
+// waves share a SIMD.
 #pragma once
 
 #include "dl_internal.h"
@@ -55,13 +57,32 @@ namespace dl {
 
 // ------------------------------------------------------------------ helpers --
 
-// Sum over the lanes of a wave64 whose lane ids differ only in bits >= log2(FROM).
+// Sum over the lanes of a wave64 whose lane ids differ only in bits >= log2(FROM)
+// (FROM a power of two), left in every lane.  Everything stays in registers:
+//   - within a 16-lane row, adding the row rotated by FROM, 2 FROM, ..., 8
+//     (DPP row_ror) leaves each lane the sum of the lanes of its row that share
+//     its low bits;
+//   - across rows, v_permlane16_swap applied to two copies of x returns rows
+//     (r0, r0, r2, r2) and (r1, r1, r3, r3), whose sum is the xor-16 sum, and
+//     v_permlane32_swap likewise gives the xor-32 sum.
+// Call with the whole wave active.
+template <int ROR> __device__ __forceinline__ float add_row_ror(float x)
+{
+    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + ROR, 0xF, 0xF, false));
+}
 template <int FROM> __device__ __forceinline__ float wave_sum_from(float x)
 {
-#pragma unroll
-    for (int off = FROM; off < 64; off <<= 1)
-        x += __shfl_xor(x, off, 64);
-    return x;
+    static_assert(FROM >= 1 && FROM <= 32 && (FROM & (FROM - 1)) == 0, "power of two");
+    if constexpr (FROM <= 1) x = add_row_ror<1>(x);
+    if constexpr (FROM <= 2) x = add_row_ror<2>(x);
+    if constexpr (FROM <= 4) x = add_row_ror<4>(x);
+    if constexpr (FROM <= 8) x = add_row_ror<8>(x);
+    if constexpr (FROM <= 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Raw buffer resources: a base, a size in bytes, and loads at a 32-bit byte
@@ -203,13 +224,15 @@ __host__ __device__ constexpr int fold_rows(int mode, int n)
          : mode == EAGER ? 1 : mode_fold(mode) ? n : 0;
 }
 constexpr int kRowTables = 8;
+// Floats per row table: d_k entries and a pad slot, rounded to 16 bytes.
+__host__ __device__ constexpr int row_table_stride(int DK) { return DK + 4; }
 // Dynamic LDS floats of the step kernel: eight per-row tables [DK], Bt
 // [bt_rows][T], F [fold_rows][DK], coefficients [2n+1], then a 16-byte aligned
 // junk slot: lanes with nothing to publish store there, which keeps the
 // publishing stores unconditional.
 __host__ __device__ constexpr int dyn_floats(int mode, int n, int DK, int T)
 {
-    return kRowTables * DK + bt_rows(mode, n) * T + fold_rows(mode, n) * DK +
+    return kRowTables * row_table_stride(DK) + bt_rows(mode, n) * T + fold_rows(mode, n) * DK +
            (mode_logged(mode) ? 2 * n + 1 : 0) + 3 + 4;
 }
 
@@ -398,18 +421,21 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
 
     const int nb = bt_rows(MODE, n);
     const int nf = merging ? n + 1 : MODE == EAGER ? 1 : FOLDS ? n : 0;
+    // Per-row tables, each TS = d_k + 4 floats: entry d_k is a pad slot that
+    // lanes past d_k write to, so one row index addresses every table.
+    constexpr int TS = row_table_stride(DK);
     float *Wq = dyn;             // read weights, q side
-    float *Wk = dyn + DK;        // read weights, k side
-    float *Rf = dyn + 2 * DK;    // fold base factor e^{Lam_f}
-    float *Lf = dyn + 3 * DK;    // fold log-decay Lam_f
-    float *Qk = dyn + 4 * DK;    // q.k (RWKV6: r.(u (.) k)) terms
-    float *Qr = dyn + 5 * DK;    // raw q (FUSED coefficient pass)
-    float *Kr = dyn + 6 * DK;    // raw k (FUSED)
-    float *Lx = dyn + 7 * DK;    // replay log-decay: Lam' (delta) / Lam_{n-1} (RWKV6) (FUSED)
-    float *Bt = dyn + kRowTables * DK;         // [nb][T] value-side factors of this tile
+    float *Wk = dyn + TS;        // read weights, k side
+    float *Rf = dyn + 2 * TS;    // fold base factor e^{Lam_f}
+    float *Lf = dyn + 3 * TS;    // fold log-decay Lam_f
+    float *Qk = dyn + 4 * TS;    // q.k (RWKV6: r.(u (.) k)) terms
+    float *Qr = dyn + 5 * TS;    // raw q (FUSED coefficient pass)
+    float *Kr = dyn + 6 * TS;    // raw k (FUSED)
+    float *Lx = dyn + 7 * TS;    // replay log-decay: Lam' (delta) / Lam_{n-1} (RWKV6) (FUSED)
+    float *Bt = dyn + kRowTables * TS;         // [nb][T] value-side factors of this tile
     float *F = Bt + nb * T;                    // [nf][DK] key-side fold coefficients
     float *cf = F + nf * DK;                   // [2n+1] c^q, c^k, kappa (LOGGED)
-    float *junk = dyn + ((kRowTables * DK + nb * T + nf * DK + (LOGGED ? 2 * n + 1 : 0) + 3) & ~3);
+    float *junk = dyn + ((kRowTables * TS + nb * T + nf * DK + (LOGGED ? 2 * n + 1 : 0) + 3) & ~3);
 
     // ------------------------------------------------------ 0. small loads --
     // Row metadata for rows i = tid + j*NT (lanes past d_k skip).
@@ -555,19 +581,20 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
         } else {
             wq = (MODE == EAGER ? 1.f : expf(mprev[j])) * mq[j];
         }
-        (ok ? Wq + i : junk)[0] = wq;
+        float *row = dyn + (ok ? i : DK); // this lane's entry of every table (or the pad)
+        row[0 * TS] = wq;
         if (DELTA)
-            (ok ? Wk + i : junk)[0] = wk;
+            row[1 * TS] = wk;
         if (OP != GDN && MAY_WRITE) {
-            (ok ? Rf + i : junk)[0] = expf(lfold);
-            (ok ? Lf + i : junk)[0] = lfold;
+            row[2 * TS] = expf(lfold);
+            row[3 * TS] = lfold;
         }
         if (KAPPA_HERE)
-            (ok ? Qk + i : junk)[0] = DELTA ? mq[j] * mk[j] : mq[j] * mu[j] * mk[j];
+            row[4 * TS] = DELTA ? mq[j] * mk[j] : mq[j] * mu[j] * mk[j];
         if (FUSED) {
-            (ok ? Qr + i : junk)[0] = mq[j];
-            (ok ? Kr + i : junk)[0] = mk[j];
-            (ok ? Lx + i : junk)[0] = OP == RWKV6 ? mprev[j] : lnew;
+            row[5 * TS] = mq[j];
+            row[6 * TS] = mk[j];
+            row[7 * TS] = OP == RWKV6 ? mprev[j] : lnew;
             if (merging)
                 (ok ? F + n * DK + i : junk)[0] = mk[j]; // this step's entry folds with k
             if (!merging && tile == 0 && ok) {          // key-side append of entry n
@@ -655,7 +682,7 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
             const int r = r0 + p * RPP;
             const float wq = Wq[r];
             const float wk = DELTA ? Wk[r] : 0.f;
-            if (KAPPA_HERE && c4 == 0)
+            if (KAPPA_HERE) // every lane sums its rows; only lane 0's class is used
                 kap += Qk[r];
             const float xs[4] = {x[p].x, x[p].y, x[p].z, x[p].w};
 #pragma unroll
@@ -709,7 +736,9 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
     if (READS && tid < LPR) {
         float y[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         float kap = 0.f;
-#pragma unroll
+        // one wave's partial sums at a time (merging launches keep the tile in
+        // registers through this, so the partials must not all be live at once)
+#pragma unroll 1
         for (int w = 0; w < NW; ++w) {
 #pragma unroll
             for (int c = 0; c < 8; ++c)
@@ -722,19 +751,21 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
             for (int c = 0; c < 8; ++c)
                 y[c] *= g;
         }
-        float rq[4] = {0.f, 0.f, 0.f, 0.f}, rk[4] = {0.f, 0.f, 0.f, 0.f};
+        // the log's replay terms sum_m c_m b_m, added straight onto the base's
+        // column sums (q side into y[0..3], k side into y[4..7])
         if (LOGGED) {
             if (STAGED)
                 kap = cf[2 * n];
+#pragma unroll 2
             for (int m = 0; m < n; ++m) {
                 const float4 b = *reinterpret_cast<const float4 *>(Bt + m * T + 4 * c4);
                 const float bs[4] = {b.x, b.y, b.z, b.w};
                 const float cq = cf[m], ck = cf[n + m];
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
-                    rq[c] = fmaf(cq, bs[c], rq[c]);
+                    y[c] = fmaf(cq, bs[c], y[c]);
                     if (DELTA)
-                        rk[c] = fmaf(ck, bs[c], rk[c]);
+                        y[4 + c] = fmaf(ck, bs[c], y[4 + c]);
                 }
             }
         }
@@ -744,11 +775,11 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             if (DELTA) {
-                bt[c] = bet * (vs[c] - y[4 + c] - rk[c]);
-                ov[c] = y[c] + rq[c] + kap * bt[c];
+                bt[c] = bet * (vs[c] - y[4 + c]);
+                ov[c] = y[c] + kap * bt[c];
             } else {
                 bt[c] = vs[c];
-                ov[c] = y[c] + rq[c] + kap * vs[c];
+                ov[c] = y[c] + kap * vs[c];
             }
         }
         *reinterpret_cast<float4 *>(a.o + (long)sh * DV + col) = make_float4(ov[0], ov[1], ov[2], ov[3]);
@@ -774,19 +805,29 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
         const float gs = OP == GDN ? expf(gnew) : 1.f;
 #pragma unroll
         for (int p = 0; p < P; ++p) {
-            const int r = r0 + p * RPP;
-            const float bf = OP == GDN ? gs : Rf[r];
-            float4 acc = make_float4(bf * x[p].x, bf * x[p].y, bf * x[p].z, bf * x[p].w);
-            for (int m = 0; m < nf; ++m) {
-                const float f = F[m * DK + r];
-                const float4 b = *reinterpret_cast<const float4 *>(Bt + m * T + 4 * c4);
-                acc.x = fmaf(f, b.x, acc.x);
-                acc.y = fmaf(f, b.y, acc.y);
-                acc.z = fmaf(f, b.z, acc.z);
-                acc.w = fmaf(f, b.w, acc.w);
-            }
-            buf_st4(tile_r, xoff, p * RPP * DV * 4, acc);
+            const float bf = OP == GDN ? gs : Rf[r0 + p * RPP];
+            x[p] = make_float4(bf * x[p].x, bf * x[p].y, bf * x[p].z, bf * x[p].w);
         }
+        // The rank-nf update in place on the tile, one entry at a time: the
+        // entry's value-side factors for this lane's columns are read once and
+        // applied to all P rows (a limited unroll keeps the entries' factors
+        // from piling up in registers).
+#pragma unroll 2
+        for (int m = 0; m < nf; ++m) {
+            const float4 b = *reinterpret_cast<const float4 *>(Bt + m * T + 4 * c4);
+            const float *Fm = F + m * DK + r0;
+#pragma unroll
+            for (int p = 0; p < P; ++p) {
+                const float f = Fm[p * RPP];
+                x[p].x = fmaf(f, b.x, x[p].x);
+                x[p].y = fmaf(f, b.y, x[p].y);
+                x[p].z = fmaf(f, b.z, x[p].z);
+                x[p].w = fmaf(f, b.w, x[p].w);
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < P; ++p)
+            buf_st4(tile_r, xoff, p * RPP * DV * 4, x[p]);
     }
 }
 
