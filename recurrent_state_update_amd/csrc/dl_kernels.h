@@ -392,7 +392,9 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
     constexpr int BS = DELTA ? 4 : ES;                     // b-log element size
     constexpr int NV = 9;                                  // 4 yq, 4 yk, kappa
     constexpr int RW = (DK + NT - 1) / NT;                 // row-table rows per lane
-    constexpr int SB = ((DL_MAX_M - 1) * (T / 4) + NT - 1) / NT; // log-shard float4 per lane
+    // log-shard float4 per lane: staged ahead of the tile's rows for the first
+    // NT/(T/4) entries (16 with 64-column tiles); longer logs take a second pass
+    constexpr int SB = ((DL_MAX_M - 1) * (T / 4) + NT - 1) / NT;
     constexpr int KPL = (DK + 63) / 64;                    // keys per lane, coefficient pass
     constexpr int EW = (8 + NW - 1) / NW;                  // entries per wave, coefficient pass
 
@@ -400,7 +402,8 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
     float *dyn = reinterpret_cast<float *>(dyn4);
     __shared__ float red[NW][LPR][NV];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6); // uniform: scalar registers
     const int c4 = tid % LPR, r0 = tid / LPR;
     // Natural block order: consecutive workgroups (dispatched round-robin over
     // the 8 XCDs) read adjacent tiles, which streams HBM faster than giving
@@ -484,20 +487,15 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
     // This tile's shard of the n logged value-side factors.
     const rsrc_t b_r = make_rsrc(static_cast<const char *>(a.blog) + (long)sh * M * DV * BS,
                                  MODE == EAGER ? 0 : n * DV * BS);
-    u32x4 bst[SB];
-#pragma unroll
-    for (int s = 0; s < SB; ++s) {
+    auto shard_load = [&](int s) { // slot idx = tid + s NT: entry m, float4 j4
         const int idx = tid + s * NT;
         const int m = idx / (T / 4), j4 = idx % (T / 4);
-        bst[s] = u32x4{(unsigned)tid, 0u, 0u, 0u}; // placeholder, stored to the junk slot
-        if (MODE != EAGER && s * NT + wave * 64 < n * (T / 4)) { // the wave holds live slots
-            const unsigned e = idx < n * (T / 4) ? (unsigned)(m * DV + tile * T + 4 * j4) : kSkipElem;
-            if (DELTA)
-                bst[s] = buf_raw4<float>(b_r, e);
-            else
-                bst[s] = buf_raw4<TIn>(b_r, e);
-        }
-    }
+        const unsigned e = idx < n * (T / 4) ? (unsigned)(m * DV + tile * T + 4 * j4) : kSkipElem;
+        return DELTA ? buf_raw4<float>(b_r, e) : buf_raw4<TIn>(b_r, e);
+    };
+    u32x4 bst = u32x4{(unsigned)tid, 0u, 0u, 0u}; // placeholder, stored to the junk slot
+    if (MODE != EAGER && wave * 64 < n * (T / 4)) // the wave holds live slots
+        bst = shard_load(0);
     // ReplayPrep's coefficients (two-stage path)
     unsigned cst = (unsigned)tid; // placeholder for lanes past 2n+1
     if (STAGED && wave * 64 < 2 * n + 1) {
@@ -558,6 +556,7 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
         mell[j] = __uint_as_float(rell[j]);
         mu[j] = __uint_as_float(ru[j]);
     }
+    float lnew_[RW]; // Lam' per row, kept for the key-side append at the end
 #pragma unroll
     for (int j = 0; j < RW; ++j) {
         const int i = tid + j * NT;
@@ -597,28 +596,24 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
             row[7 * TS] = OP == RWKV6 ? mprev[j] : lnew;
             if (merging)
                 (ok ? F + n * DK + i : junk)[0] = mk[j]; // this step's entry folds with k
-            if (!merging && tile == 0 && ok) {          // key-side append of entry n
-                // a_n = k as whole 32-bit words: for bf16 the even lane stores
-                // the raw word holding k[i] and k[i+1]
-                if (sizeof(TIn) == 4 || (i & 1) == 0)
-                    *reinterpret_cast<unsigned *>(static_cast<TIn *>(a.alog) + ((long)sh * M + n) * DK + i) = rk_[j];
-                if (OP != GDN)
-                    L[(long)n * DK + i] = lnew;
-            }
         }
+        lnew_[j] = lnew;
         if (MODE == EAGER)
             (ok ? F + i : junk)[0] = mk[j]; // the only entry folds with k
     }
-    if (OP == GDN && FUSED && !merging && tile == 0 && tid == 0)
-        L[n] = gnew;
     if (MODE != EAGER) {
-#pragma unroll
-        for (int s = 0; s < SB; ++s) {
+        auto shard_store = [&](int s, u32x4 raw) {
             const int idx = tid + s * NT;
             const int m = idx / (T / 4), j4 = idx % (T / 4);
             float *dst = idx < n * (T / 4) ? Bt + m * T + 4 * j4 : junk;
-            *reinterpret_cast<float4 *>(dst) = DELTA ? cvt4<float>(bst[s]) : cvt4<TIn>(bst[s]);
-        }
+            *reinterpret_cast<float4 *>(dst) = DELTA ? cvt4<float>(raw) : cvt4<TIn>(raw);
+        };
+        shard_store(0, bst);
+        // a log longer than one staging pass: the rest now (these loads queue
+        // behind the tile's rows, so only such long logs wait for them here)
+#pragma unroll 1
+        for (int s = 1; s < SB && s * NT < n * (T / 4); ++s)
+            shard_store(s, shard_load(s));
     }
     if (STAGED)
         (tid < 2 * n + 1 ? cf + tid : junk)[0] = __uint_as_float(cst);
@@ -732,17 +727,20 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
         }
     }
 
-    // ------------------------ 6. finalise this tile's outputs (lanes < LPR)
-    if (READS && tid < LPR) {
+    // ------------------------ 6. finalise this tile's outputs (wave 0)
+    // Lane c + LPR g of wave 0 (g < G) takes column group c's partial sums of
+    // waves g, g+G, ... and the replay terms of log entries g, g+G, ...; a
+    // register reduction over g combines them, then lanes < LPR finish.
+    if (READS && wave == 0) {
+        constexpr int G = 64 / LPR;
+        const int grp = lane / LPR;
         float y[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         float kap = 0.f;
-        // one wave's partial sums at a time (merging launches keep the tile in
-        // registers through this, so the partials must not all be live at once)
 #pragma unroll 1
-        for (int w = 0; w < NW; ++w) {
+        for (int w = grp; w < NW; w += G) {
 #pragma unroll
             for (int c = 0; c < 8; ++c)
-                y[c] += red[w][tid][c];
+                y[c] += red[w][c4][c];
             kap += red[w][0][8];
         }
         if (OP == GDN) {
@@ -751,13 +749,11 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
             for (int c = 0; c < 8; ++c)
                 y[c] *= g;
         }
-        // the log's replay terms sum_m c_m b_m, added straight onto the base's
-        // column sums (q side into y[0..3], k side into y[4..7])
+        // the log's replay terms sum_m c_m b_m, added onto the base's column
+        // sums (q side into y[0..3], k side into y[4..7])
         if (LOGGED) {
-            if (STAGED)
-                kap = cf[2 * n];
 #pragma unroll 2
-            for (int m = 0; m < n; ++m) {
+            for (int m = grp; m < n; m += G) {
                 const float4 b = *reinterpret_cast<const float4 *>(Bt + m * T + 4 * c4);
                 const float bs[4] = {b.x, b.y, b.z, b.w};
                 const float cq = cf[m], ck = cf[n + m];
@@ -769,34 +765,64 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
                 }
             }
         }
-        const float4 vv = cvt4<TIn>(vraw);
-        const float vs[4] = {vv.x, vv.y, vv.z, vv.w};
-        float bt[4], ov[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            if (DELTA) {
-                bt[c] = bet * (vs[c] - y[4 + c]);
-                ov[c] = y[c] + kap * bt[c];
-            } else {
-                bt[c] = vs[c];
-                ov[c] = y[c] + kap * vs[c];
+        for (int c = 0; c < 8; ++c)
+            if (DELTA || c < 4)
+                y[c] = wave_sum_from<LPR>(y[c]);
+        if (KAPPA_HERE)
+            kap = wave_sum_from<LPR>(kap);
+        if (STAGED)
+            kap = cf[2 * n];
+        if (lane < LPR) {
+            const float4 vv = cvt4<TIn>(vraw);
+            const float vs[4] = {vv.x, vv.y, vv.z, vv.w};
+            float bt[4], ov[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                if (DELTA) {
+                    bt[c] = bet * (vs[c] - y[4 + c]);
+                    ov[c] = y[c] + kap * bt[c];
+                } else {
+                    bt[c] = vs[c];
+                    ov[c] = y[c] + kap * vs[c];
+                }
+            }
+            *reinterpret_cast<float4 *>(a.o + (long)sh * DV + col) = make_float4(ov[0], ov[1], ov[2], ov[3]);
+            if (LOGGED && !merging) { // value-side append of entry n (a merge empties the log)
+                const long off = ((long)sh * M + n) * DV + col;
+                if (DELTA) {
+                    *reinterpret_cast<float4 *>(static_cast<float *>(a.blog) + off) =
+                        make_float4(bt[0], bt[1], bt[2], bt[3]);
+                } else {
+                    TIn *bl = static_cast<TIn *>(a.blog) + off;
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        bl[c] = to_in<TIn>(vs[c]);
+                }
+            }
+            if (writes)
+                *reinterpret_cast<float4 *>(Bt + (nb - 1) * T + 4 * c4) = make_float4(bt[0], bt[1], bt[2], bt[3]);
+        }
+    }
+
+    // Key-side append of entry n (a_n = k, Lam_n = Lam'), by tile 0, issued
+    // last: stores count against the same wait counter as loads, so a store
+    // issued earlier would hold up the wait for the tile's rows.
+    if (FUSED && !merging && tile == 0) {
+#pragma unroll
+        for (int j = 0; j < RW; ++j) {
+            const int i = tid + j * NT;
+            if (i < DK) {
+                // a_n = k as whole 32-bit words: for bf16 the even lane stores
+                // the raw word holding k[i] and k[i+1]
+                if (sizeof(TIn) == 4 || (i & 1) == 0)
+                    *reinterpret_cast<unsigned *>(static_cast<TIn *>(a.alog) + ((long)sh * M + n) * DK + i) = rk_[j];
+                if (OP != GDN)
+                    L[(long)n * DK + i] = lnew_[j];
             }
         }
-        *reinterpret_cast<float4 *>(a.o + (long)sh * DV + col) = make_float4(ov[0], ov[1], ov[2], ov[3]);
-        if (LOGGED && !merging) { // value-side append of entry n (a merge empties the log)
-            const long off = ((long)sh * M + n) * DV + col;
-            if (DELTA) {
-                *reinterpret_cast<float4 *>(static_cast<float *>(a.blog) + off) =
-                    make_float4(bt[0], bt[1], bt[2], bt[3]);
-            } else {
-                TIn *bl = static_cast<TIn *>(a.blog) + off;
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    bl[c] = to_in<TIn>(vs[c]);
-            }
-        }
-        if (writes)
-            *reinterpret_cast<float4 *>(Bt + (nb - 1) * T + 4 * c4) = make_float4(bt[0], bt[1], bt[2], bt[3]);
+        if (OP == GDN && tid == 0)
+            L[n] = gnew;
     }
 
     // --------------------------------------- 7. fold and write the tile once
