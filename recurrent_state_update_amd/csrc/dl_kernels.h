@@ -621,51 +621,55 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
 
     // ------------- 3. FUSED: this wave's replay coefficients (and fold rows)
     if (FUSED) {
-        for (int m0 = 0; m0 < n; m0 += NW * EW) {
-            if (m0 > 0) { // a log longer than one pass: load this pass's entries
+        // one log entry m from its raw words: c^q_m, c^k_m and (merging) the
+        // entry's fold row
+        auto coef_entry = [&](int m, const unsigned *am_raw, const unsigned *lm_raw, float gm) {
+            // GDN: the entry's scalar factor e^{Lam' - Lam_m}
+            const float g = OP == GDN ? expf(gnew - gm) : 1.f;
+            float sq = 0.f, sk = 0.f;
 #pragma unroll
-                for (int e = 0; e < EW; ++e) {
-                    const int m = m0 + wave + NW * e;
-                    eg[e] = (OP == GDN && m < n) ? L[m] : 0.f;
-#pragma unroll
-                    for (int c = 0; c < KPL; ++c) {
-                        const int i = lane + 64 * c;
-                        const unsigned ei = (m < n && i < DK) ? (unsigned)(m * DK + i) : kSkipElem;
-                        ea[e][c] = buf_raw1<TIn>(a_r, ei);
-                        el[e][c] = OP != GDN ? buf_raw1<float>(L_r, ei) : 0u;
-                    }
-                }
-            }
-#pragma unroll
-            for (int e = 0; e < EW; ++e) {
-                const int m = m0 + wave + NW * e;
-                if (m >= n)
-                    break; // uniform over the wave
-                // GDN: the entry's scalar factor e^{Lam' - Lam_m}
-                const float g = OP == GDN ? expf(gnew - eg[e]) : 1.f;
-                float sq = 0.f, sk = 0.f;
-#pragma unroll
-                for (int c = 0; c < KPL; ++c) {
-                    const int i = lane + 64 * c;
-                    if (i >= DK)
-                        continue;
-                    const float am = cvt1<TIn>(ea[e][c], i), lm = __uint_as_float(el[e][c]);
-                    // e^{Lam_x,i - Lam_m,i} a_m,i (GDN: scalar factor applied after the sum)
-                    const float f = OP == GDN ? am : expf(Lx[i] - lm) * am;
-                    sq = fmaf(f, Qr[i], sq);
-                    if (DELTA)
-                        sk = fmaf(f, Kr[i], sk);
-                    if (merging) // fold row: e^{Lam' - Lam_m} a_m
-                        F[m * DK + i] = OP == GDN ? g * am : OP == KDA ? f : expf(Lf[i] - lm) * am;
-                }
-                sq = wave_sum_from<1>(sq);
+            for (int c = 0; c < KPL; ++c) {
+                const int i = lane + 64 * c;
+                if (i >= DK)
+                    continue;
+                const float am = cvt1<TIn>(am_raw[c], i), lm = __uint_as_float(lm_raw[c]);
+                // e^{Lam_x,i - Lam_m,i} a_m,i (GDN: scalar factor applied after the sum)
+                const float f = OP == GDN ? am : expf(Lx[i] - lm) * am;
+                sq = fmaf(f, Qr[i], sq);
                 if (DELTA)
-                    sk = wave_sum_from<1>(sk);
-                if (lane == 0) {
-                    cf[m] = g * sq;
-                    cf[n + m] = g * sk;
-                }
+                    sk = fmaf(f, Kr[i], sk);
+                if (merging) // fold row: e^{Lam' - Lam_m} a_m
+                    F[m * DK + i] = OP == GDN ? g * am : OP == KDA ? f : expf(Lf[i] - lm) * am;
             }
+            sq = wave_sum_from<1>(sq);
+            if (DELTA)
+                sk = wave_sum_from<1>(sk);
+            if (lane == 0) {
+                cf[m] = g * sq;
+                cf[n + m] = g * sk;
+            }
+        };
+        // entries wave, wave + NW, ... below NW*EW: loaded ahead of the tile
+#pragma unroll
+        for (int e = 0; e < EW; ++e) {
+            const int m = wave + NW * e;
+            if (m >= n)
+                break; // uniform over the wave
+            coef_entry(m, ea[e], el[e], eg[e]);
+        }
+        // a longer log: one entry per wave at a time, loaded here (behind the
+        // tile's rows, so only such long logs wait for them)
+#pragma unroll 1
+        for (int m = NW * EW + wave; m < n; m += NW) {
+            unsigned am_raw[KPL], lm_raw[KPL];
+#pragma unroll
+            for (int c = 0; c < KPL; ++c) {
+                const int i = lane + 64 * c;
+                const unsigned ei = i < DK ? (unsigned)(m * DK + i) : kSkipElem;
+                am_raw[c] = buf_raw1<TIn>(a_r, ei);
+                lm_raw[c] = OP != GDN ? buf_raw1<float>(L_r, ei) : 0u;
+            }
+            coef_entry(m, am_raw, lm_raw, OP == GDN ? L[m] : 0.f);
         }
     }
 
@@ -752,7 +756,7 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
         // the log's replay terms sum_m c_m b_m, added onto the base's column
         // sums (q side into y[0..3], k side into y[4..7])
         if (LOGGED) {
-#pragma unroll 2
+#pragma unroll 1
             for (int m = grp; m < n; m += G) {
                 const float4 b = *reinterpret_cast<const float4 *>(Bt + m * T + 4 * c4);
                 const float bs[4] = {b.x, b.y, b.z, b.w};
