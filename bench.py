@@ -5,6 +5,9 @@
 One "step" is one DeltaLog decode step (dl_decode_step: one launch of the
 step kernel, which also folds the log into the base on every M-th step) for
 all B*H slot-heads of one state, with its inputs already resident in HBM.
+The timed steps are replayed from a HIP graph of whole merge cycles, as a
+decode loop runs on the GPU; the same steps as direct launches are reported
+beside them.
 The default workload is GDN B=64 H=32 d_k=d_v=128 M=8 with bf16 q/k/v and an
 fp32 state.  With --rotate R (default 4) the steps go round R independent
 states, as the layers of a model do, so the 512 MiB working set exceeds the
@@ -13,9 +16,9 @@ single-state figure (cache-resident) is reported beside it.
 
 Prints ONE JSON line with the throughput in (token*head)/s, the roofline of
 the step kernel (algorithmic bytes per launch / mean launch time measured
-with HIP events on the launch stream), the same-GPU eager and two-stage
-figures, the other operators' workloads, and the fp64 CPU oracle timed on a
-bounded sample.
+with HIP events on the replay stream), the direct-launch, same-GPU eager,
+two-stage and per-slot figures, the other operators' workloads, and the fp64
+CPU oracle timed on a bounded sample.
 """
 from __future__ import annotations
 
@@ -184,37 +187,85 @@ def run_deltalog(w, inp, sts, K: int, W: int, instrument: bool, path: str = "fus
     return wall, launches, prep
 
 
-def run_graph(w, inp, sts, K: int):
-    """The same steps replayed from a HIP graph: one merge cycle of every
-    state (R*M launches, each state's steps interleaved as in the timed loop)
-    captured once, replayed K/(R*M) times.  Returns wall ms per step."""
+def graph_len(period: int, pool: int, K: int) -> int:
+    """Launches per captured graph: a whole number of schedule periods that
+    also walks the whole input pool when that divides K, else one period."""
+    import math
+    full = period * pool // math.gcd(period, pool)
+    if K % full == 0:
+        return full
+    if K % period == 0:
+        return period
+    raise SystemExit(f"--steps {K} must be a multiple of {period} (states x merge interval)")
+
+
+def time_graph(launch, G: int, K: int, W: int) -> float:
+    """Capture launch(0..G-1) as one HIP graph, replay it ceil(W/G) times
+    untimed, then K/G times between two HIP events on the replay stream.
+    Returns ms per launch."""
     import torch
-    import recurrent_state_update_amd as rsu
-    R = len(sts)
-    pool = inp["q"].shape[0]
-    ptrs = [_ptrs(inp, s) for s in range(pool)]
-    o = torch.empty(w.B, w.H, w.dv, device="cuda")
-    for st in sts:  # start every state at an empty log
-        st.merge()
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         sp = torch.cuda.current_stream().cuda_stream
-        for i in range(R * w.M):
-            q, k, v, beta, ld = ptrs[i % pool]
-            if rsu._lib.dl_decode_step(sts[i % R]._h, q, k, v, beta, ld, o.data_ptr(), sp) != 0:
-                raise RuntimeError("dl_decode_step failed under capture")
-    reps = max(1, K // (R * w.M))
-    g.replay()
+        for i in range(G):
+            launch(i, sp)
+    for _ in range(max(1, -(-W // G))):
+        g.replay()
     torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for _ in range(reps):
+    t0.record(stream)
+    for _ in range(K // G):
         g.replay()
-    t1.record()
+    t1.record(stream)
     torch.cuda.synchronize()
-    return t0.elapsed_time(t1) / (reps * R * w.M)
+    return t0.elapsed_time(t1) / K
+
+
+def run_graph(w, inp, sts, K: int, W: int):
+    """DeltaLog steps replayed from a HIP graph: G launches (state i % R,
+    inputs i % pool; whole merge cycles of every state) captured once and
+    replayed.  Every state starts from an empty log.  Returns ms per step."""
+    import recurrent_state_update_amd as rsu
+    import torch
+    R = len(sts)
+    pool = inp["q"].shape[0]
+    ptrs = [_ptrs(inp, s) for s in range(pool)]
+    o = torch.empty(w.B, w.H, w.dv, device="cuda")
+    for st in sts:
+        st.merge()
+    hs = [st._h for st in sts]
+
+    def launch(i, sp):
+        q, k, v, beta, ld = ptrs[i % pool]
+        if rsu._lib.dl_decode_step(hs[i % R], q, k, v, beta, ld, o.data_ptr(), sp) != 0:
+            raise RuntimeError("dl_decode_step failed under capture")
+
+    return time_graph(launch, graph_len(R * w.M, pool, K), K, W)
+
+
+def run_eager_graph(w, inp, bases, u_dev, K: int, W: int):
+    """The eager step on R dense states, replayed from a HIP graph the same
+    way.  Returns ms per step."""
+    import recurrent_state_update_amd as rsu
+    import torch
+    R = len(bases)
+    pool = inp["q"].shape[0]
+    ptrs = [_ptrs(inp, s) for s in range(pool)]
+    o = torch.empty(w.B, w.H, w.dv, device="cuda")
+    bptr = [b.data_ptr() for b in bases]
+    uptr = None if u_dev is None else u_dev.data_ptr()
+    opi, dti = rsu.OPS[w.op], rsu.DTYPES[inp["q"].dtype]
+
+    def launch(i, sp):
+        q, k, v, beta, ld = ptrs[i % pool]
+        if rsu._lib.dl_eager_step(opi, w.B, w.H, w.dk, w.dv, dti, bptr[i % R], q, k, v, beta, ld,
+                                  uptr, o.data_ptr(), sp) != 0:
+            raise RuntimeError("dl_eager_step failed under capture")
+
+    return time_graph(launch, graph_len(R, pool, K), K, W)
 
 
 def run_per_slot(w, inp, R: int, K: int, W: int):
@@ -366,67 +417,73 @@ def measured_traffic():
     return t.get("hbm_bytes_per_launch")
 
 
+def cycle_launch_bytes(w) -> float:
+    """Mean algorithmic bytes per launch over one merge cycle (log lengths
+    0..M-1, the last launch merging)."""
+    return sum(step_launch_bytes(w, n, n + 1 == w.M) for n in range(w.M)) / w.M
+
+
 def bench_workload(w, K, W, R, pool, with_eager=True, with_staged=True):
-    """Time workload w.  The timed region holds only K back-to-back launches of
-    the step kernel (one per step, HIP events at its two ends on the launch
-    stream): its length / K is both the step time and the kernel's mean launch
-    duration (dispatch gaps included).  A second, per-launch event-bracketed
-    pass splits append and merge launches (each bracket adds event overhead)."""
+    """Time workload w.  Headline: K steps replayed from a HIP graph of whole
+    merge cycles (the way a decode loop runs on the GPU), timed with HIP events
+    on the replay stream; K / region length is the step rate and region length
+    / K the mean launch duration of the step kernel (gaps included).  Beside it:
+    the same steps as K direct launches, a per-launch event-bracketed pass that
+    splits append and merge launches (each bracket adds event overhead), the
+    two-stage path, per-slot logs, and the eager step (graph-replayed too)."""
     import torch
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     inp = stage_inputs(w, pool, dt)
     sts, base0, u_dev = make_states(w, R, dt)
     res = {}
-    ns0 = [st.log_len for st in sts]
-    wall, _, _ = run_deltalog(w, inp, sts, K, W, instrument=False, path="fused")
-    # log length seen by each timed launch (the schedule is deterministic)
-    ns = []
-    cur = list(ns0)
-    for i in range(W + K):
-        r = i % R
-        if i >= W:
-            ns.append(cur[r])
-        cur[r] = 0 if cur[r] + 1 == w.M else cur[r] + 1
-    tot_bytes = sum(step_launch_bytes(w, n, n + 1 == w.M) for n in ns)
-    avg_ms = wall / K
-    res["wall_ms"] = wall
-    res["value"] = w.BH * K / (wall * 1e-3)
-    achieved = tot_bytes / K / (avg_ms * 1e-3) / 1e9
+    gms = run_graph(w, inp, sts, K, W)
+    per_launch = cycle_launch_bytes(w)
+    res["wall_ms"] = gms * K
+    res["value"] = w.BH / (gms * 1e-3)
+    achieved = per_launch / (gms * 1e-3) / 1e9
     res["roofline"] = dict(
         bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
         frac=round(achieved / PEAK_HBM_GBS, 4), traffic=None,
         kernel="step_kernel, one-launch append/merge modes (dl_decode_step)",
-        avg_launch_us=round(avg_ms * 1e3, 2), bytes_per_launch=int(tot_bytes / K))
+        avg_launch_us=round(gms * 1e3, 2), bytes_per_launch=int(per_launch))
+    res["modelled_step_GBs"] = round(modelled_step_bytes(w) / (gms * 1e-3) / 1e9, 1)
+    # the same steps as direct launches
+    for st in sts:
+        st.merge()
+    wall, _, _ = run_deltalog(w, inp, sts, K, W, instrument=False, path="fused")
+    res["direct_launch"] = dict(value=round(w.BH * K / (wall * 1e-3), 1), ms_per_step=round(wall / K, 5),
+                                achieved_GBs=round(per_launch / (wall / K * 1e-3) / 1e9, 1))
     _, launches, _ = run_deltalog(w, inp, sts, K, W, instrument=True, path="fused")
     app = [x[0] for x in launches if not x[2]]
     mer = [x[0] for x in launches if x[2]]
     res["roofline"]["event_bracketed_us"] = dict(append=round(1e3 * sum(app) / max(len(app), 1), 2),
                                                  merge=round(1e3 * sum(mer) / max(len(mer), 1), 2))
-    res["modelled_step_GBs"] = round(modelled_step_bytes(w) / (avg_ms * 1e-3) / 1e9, 1)
     if R > 1:
         one, _, _ = run_deltalog(w, inp, sts[:1], K, W, instrument=False)
         res["single_state_value"] = round(w.BH * K / (one * 1e-3), 1)
     pw, pbytes = run_per_slot(w, inp, R, K, W)
     res["per_slot"] = dict(value=round(w.BH * K / (pw * 1e-3), 1), ms_per_step=round(pw / K, 5),
                            achieved_GBs=round(pbytes / (pw * 1e-3) / 1e9, 1),
-                           frac=round(pbytes / (pw * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
-    gms = run_graph(w, inp, sts, K)
-    res["graph_replay"] = dict(value=round(w.BH / (gms * 1e-3), 1), ms_per_step=round(gms, 5))
+                           frac=round(pbytes / (pw * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                           launch="direct")
     if with_staged:
         sw, _, _ = run_deltalog(w, inp, sts, K, W, instrument=False, path="staged")
         _, sl, sp = run_deltalog(w, inp, sts, K, W, instrument=True, path="staged")
         res["two_stage"] = dict(value=round(w.BH * K / (sw * 1e-3), 1), ms_per_step=round(sw / K, 5),
+                                launch="direct",
                                 event_bracketed_us=dict(
                                     append_decode=round(1e3 * sum(x[0] for x in sl) / len(sl), 2),
                                     replay_prep=round(1e3 * sum(sp) / len(sp), 2)))
     if with_eager:
         bases = [base0.clone() for _ in range(R)]
+        ems = run_eager_graph(w, inp, bases, u_dev, K, W)
         ew, _ = run_eager(w, inp, bases, u_dev, K, W, instrument=False)
-        eavg = ew / K
         res["eager_same_gpu"] = dict(
-            value=round(w.BH * K / (ew * 1e-3), 1), ms_per_step=round(eavg, 5),
-            achieved_GBs=round(eager_launch_bytes(w) / (eavg * 1e-3) / 1e9, 1),
-            deltalog_speedup=round(ew / wall, 3))
+            value=round(w.BH / (ems * 1e-3), 1), ms_per_step=round(ems, 5),
+            achieved_GBs=round(eager_launch_bytes(w) / (ems * 1e-3) / 1e9, 1),
+            deltalog_speedup=round(ems / gms, 3),
+            direct_launch_ms_per_step=round(ew / K, 5),
+            deltalog_speedup_direct=round(ew / wall, 3))
     for st in sts:
         st.close()
     del inp, sts
@@ -532,7 +589,7 @@ def main():
         "cpu_baseline": cpu,
         "modelled_step_GBs": res["modelled_step_GBs"],
         "single_state_value": res.get("single_state_value"),
-        "graph_replay": res.get("graph_replay"),
+        "direct_launch": res.get("direct_launch"),
         "per_slot": res.get("per_slot"),
         "two_stage": res.get("two_stage"),
         "eager_same_gpu": res.get("eager_same_gpu"),
