@@ -352,3 +352,51 @@ def test_per_slot_logs_continuous_batching(orc, op, M):
     assert checked >= B
     assert worst_o < FP32_TOL and worst_S < FP32_TOL
     st.close()
+
+
+@needs_gpu
+@pytest.mark.parametrize("wid", [1, 2, 3])
+def test_full_size_graph_replay(orc, wid):
+    """The launch configuration the benchmark times: dl_decode_step at the
+    workload's full size, one merge cycle captured in a HIP graph and replayed
+    for two cycles with fresh inputs copied into the captured buffers.  Every
+    output and the base after each cycle are checked on 48 sampled slot-heads
+    against the oracle."""
+    import recurrent_state_update_amd as rsu
+    w = synth.WORKLOADS[wid]
+    M = w.M
+    idx = sample_slot_heads(w.BH, 48, seed=wid)
+    X0, u = synth.initial(w)
+    dt = in_dtype(w)
+    base = dev(X0)
+    st = rsu.DeltaLogState(w.op, w.B, w.H, w.dk, w.dv, M, dtype=dt, base=base, u=dev(u))
+    static = [{k: dev(v, dt if k in ("q", "k", "v") else torch.float32) for k, v in synth.step(w, t).items()}
+              for t in range(M)]
+    outs = [torch.empty(w.B, w.H, w.dv, device="cuda") for _ in range(M)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for t in range(M):
+            s = static[t]
+            st.step(s["q"], s["k"], s["v"], s["beta"], s["ld"], o=outs[t])
+    assert st.log_len == 0
+    X = X0.reshape(w.BH, w.dk, w.dv)[idx].astype(np.float64)[None].copy()
+    u_sub = None if u is None else u[idx % w.H].astype(np.float64)
+    sel = torch.from_numpy(idx).cuda()
+    worst_o = worst_S = 0.0
+    for cycle in range(2):
+        inputs = [synth.step(w, cycle * M + t) for t in range(M)]
+        for t in range(M):
+            for k_, v_ in inputs[t].items():
+                if v_ is not None:
+                    static[t][k_].copy_(dev(v_, dt if k_ in ("q", "k", "v") else torch.float32))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for t in range(M):
+            sub = synth.subset(inputs[t], idx)
+            o_ref = orc.eager_step(w.op, X, sub["q"], sub["k"], sub["v"], sub["beta"], sub["ld"], u_sub)
+            worst_o = max(worst_o, rel(outs[t].reshape(w.BH, w.dv)[sel].cpu().numpy(), o_ref[0]))
+        worst_S = max(worst_S, rel(base.reshape(w.BH, w.dk, w.dv)[sel].cpu().numpy(), X[0]))
+    print(f"[w{wid} full-size graph replay] worst o={worst_o:.2e} S={worst_S:.2e}", flush=True)
+    st.close()
+    assert worst_o < FP32_TOL and worst_S < FP32_TOL
