@@ -173,12 +173,14 @@ def dl_status_string(st) -> str:
 
 # ------------------------------------------------------------ torch helpers --
 
-def _want(t, name, dtype, shape):
+def _want(t, name, dtype, shape, device=None):
     if t is None:
         raise ValueError(f"{name} is required")
     if not t.is_cuda or t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
         raise ValueError(f"{name}: want contiguous {dtype} {tuple(shape)} on the GPU, got "
                          f"{t.dtype} {tuple(t.shape)} on {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the state on {device}")
 
 
 class DeltaLogState:
@@ -202,7 +204,7 @@ class DeltaLogState:
         # 256-byte aligned workspace (torch's caching allocator aligns to 512)
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=base.device)
         if op == "rwkv6":
-            _want(u, "u", torch.float32, (H, d_k))
+            _want(u, "u", torch.float32, (H, d_k), base.device)
         self.u = u
         st, h = dl_state_create(B, H, d_k, d_v, M, opi, dti, base, self.workspace, u)
         _check(st, "dl_state_create")
@@ -211,16 +213,17 @@ class DeltaLogState:
     # validation of per-step tensors
     def _inputs(self, q, k, v, beta, log_decay, o):
         B, H, dk, dv = self.B, self.H, self.d_k, self.d_v
-        _want(q, "q", self.dtype, (B, H, dk))
-        _want(k, "k", self.dtype, (B, H, dk))
-        _want(v, "v", self.dtype, (B, H, dv))
+        dev = self.base.device
+        _want(q, "q", self.dtype, (B, H, dk), dev)
+        _want(k, "k", self.dtype, (B, H, dk), dev)
+        _want(v, "v", self.dtype, (B, H, dv), dev)
         if self.op != "rwkv6":
-            _want(beta, "beta", torch.float32, (B, H))
+            _want(beta, "beta", torch.float32, (B, H), dev)
         if log_decay is not None:
-            _want(log_decay, "log_decay", torch.float32, (B, H) if self.op == "gdn" else (B, H, dk))
+            _want(log_decay, "log_decay", torch.float32, (B, H) if self.op == "gdn" else (B, H, dk), dev)
         if o is None:
-            o = torch.empty(B, H, dv, dtype=torch.float32, device=q.device)
-        _want(o, "o", torch.float32, (B, H, dv))
+            o = torch.empty(B, H, dv, dtype=torch.float32, device=dev)
+        _want(o, "o", torch.float32, (B, H, dv), dev)
         return o
 
     def step(self, q, k, v, beta, log_decay, o=None, stream=None):
@@ -254,6 +257,9 @@ class DeltaLogState:
         _check(dl_state_enable_slots(self._h, stream), "dl_state_enable_slots")
 
     def admit(self, slot: int, stream=None):
+        """Start a new request in ``slot``: write its initial state into
+        ``base[slot]`` first (on the same stream), then admit; the slot's
+        pending log is dropped."""
         _check(dl_slot_admit(self._h, slot, stream), "dl_slot_admit")
 
     def merge_slot(self, slot: int, stream=None):
@@ -281,12 +287,19 @@ def eager_step(op: str, S, q, k, v, beta, log_decay, u=None, o=None, stream=None
     """The eager baseline: one step that reads and rewrites S [B,H,d_k,d_v]."""
     B, H, dk, dv = S.shape
     dtype = q.dtype
+    dev = S.device
     _want(S, "S", torch.float32, (B, H, dk, dv))
-    _want(q, "q", dtype, (B, H, dk))
-    _want(k, "k", dtype, (B, H, dk))
-    _want(v, "v", dtype, (B, H, dv))
+    _want(q, "q", dtype, (B, H, dk), dev)
+    _want(k, "k", dtype, (B, H, dk), dev)
+    _want(v, "v", dtype, (B, H, dv), dev)
+    if op != "rwkv6":
+        _want(beta, "beta", torch.float32, (B, H), dev)
+    else:
+        _want(u, "u", torch.float32, (H, dk), dev)
+    _want(log_decay, "log_decay", torch.float32, (B, H) if op == "gdn" else (B, H, dk), dev)
     if o is None:
-        o = torch.empty(B, H, dv, dtype=torch.float32, device=S.device)
+        o = torch.empty(B, H, dv, dtype=torch.float32, device=dev)
+    _want(o, "o", torch.float32, (B, H, dv), dev)
     _check(dl_eager_step(OPS[op], B, H, dk, dv, DTYPES[dtype], S, q, k, v, beta, log_decay, u, o,
                          stream), "dl_eager_step")
     return o

@@ -175,3 +175,13 @@ def test_per_slot_calls_validate_before_any_launch():
         assert rsu.dl_state_enable_slots(None, s) == INVALID
     finally:
         rsu.dl_state_destroy(h)
+
+
+def test_binding_validates_eager_inputs():
+    """The eager wrapper checks every tensor before the C call (no GPU: the
+    first mismatch raises)."""
+    import torch
+    S = torch.zeros(1, 2, 16, 16)
+    q = torch.zeros(1, 2, 16)
+    with pytest.raises(ValueError):
+        rsu.eager_step("gdn", S, q, q, q, None, None)
