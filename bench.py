@@ -423,7 +423,7 @@ def cycle_launch_bytes(w) -> float:
     return sum(step_launch_bytes(w, n, n + 1 == w.M) for n in range(w.M)) / w.M
 
 
-def bench_workload(w, K, W, R, pool, with_eager=True, with_staged=True):
+def bench_workload(w, K, W, R, pool, with_eager=True, with_staged=True, quick=False):
     """Time workload w.  Headline: K steps replayed from a HIP graph of whole
     merge cycles (the way a decode loop runs on the GPU), timed with HIP events
     on the replay stream; K / region length is the step rate and region length
@@ -447,25 +447,31 @@ def bench_workload(w, K, W, R, pool, with_eager=True, with_staged=True):
         kernel="step_kernel, one-launch append/merge modes (dl_decode_step)",
         avg_launch_us=round(gms * 1e3, 2), bytes_per_launch=int(per_launch))
     res["modelled_step_GBs"] = round(modelled_step_bytes(w) / (gms * 1e-3) / 1e9, 1)
+    if quick:  # counter runs: the headline and the eager baseline only
+        with_staged = False
     # the same steps as direct launches
     for st in sts:
         st.merge()
     wall, _, _ = run_deltalog(w, inp, sts, K, W, instrument=False, path="fused")
+    if quick:
+        launches = []
+    else:
+        _, launches, _ = run_deltalog(w, inp, sts, K, W, instrument=True, path="fused")
     res["direct_launch"] = dict(value=round(w.BH * K / (wall * 1e-3), 1), ms_per_step=round(wall / K, 5),
                                 achieved_GBs=round(per_launch / (wall / K * 1e-3) / 1e9, 1))
-    _, launches, _ = run_deltalog(w, inp, sts, K, W, instrument=True, path="fused")
     app = [x[0] for x in launches if not x[2]]
     mer = [x[0] for x in launches if x[2]]
     res["roofline"]["event_bracketed_us"] = dict(append=round(1e3 * sum(app) / max(len(app), 1), 2),
                                                  merge=round(1e3 * sum(mer) / max(len(mer), 1), 2))
-    if R > 1:
+    if R > 1 and not quick:
         one, _, _ = run_deltalog(w, inp, sts[:1], K, W, instrument=False)
         res["single_state_value"] = round(w.BH * K / (one * 1e-3), 1)
-    pw, pbytes = run_per_slot(w, inp, R, K, W)
-    res["per_slot"] = dict(value=round(w.BH * K / (pw * 1e-3), 1), ms_per_step=round(pw / K, 5),
-                           achieved_GBs=round(pbytes / (pw * 1e-3) / 1e9, 1),
-                           frac=round(pbytes / (pw * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                           launch="direct")
+    if not quick:
+        pw, pbytes = run_per_slot(w, inp, R, K, W)
+        res["per_slot"] = dict(value=round(w.BH * K / (pw * 1e-3), 1), ms_per_step=round(pw / K, 5),
+                               achieved_GBs=round(pbytes / (pw * 1e-3) / 1e9, 1),
+                               frac=round(pbytes / (pw * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                               launch="direct")
     if with_staged:
         sw, _, _ = run_deltalog(w, inp, sts, K, W, instrument=False, path="staged")
         _, sl, sp = run_deltalog(w, inp, sts, K, W, instrument=True, path="staged")
@@ -504,6 +510,8 @@ def main():
     ap.add_argument("--pool", type=int, default=None, help="distinct input steps staged")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-others", action="store_true", help="skip the KDA / RWKV6 workloads")
+    ap.add_argument("--quick", action="store_true",
+                    help="the headline and the eager baseline only (for counter runs)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB, 10 times (the "
                          "reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -546,7 +554,7 @@ def main():
             w = w.with_(M=args.M)
     K, W, R = args.steps, args.warmup, args.rotate
     pool = args.pool or min(w.steps, 256 if w.B <= 128 else 64)
-    res = bench_workload(w, K, W, R, pool)
+    res = bench_workload(w, K, W, R, pool, quick=args.quick)
     traffic = measured_traffic() if (args.workload == 1 and not args.M) else None
     res["roofline"]["traffic"] = traffic
     log(f"{w.describe()}: {res['wall_ms'] / K * 1e3:.2f} us/step")
