@@ -117,6 +117,14 @@ __device__ __forceinline__ void buf_st4(rsrc_t r, unsigned off, unsigned soff, f
 {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, soff, 0);
 }
+// Streaming store of a state tile: used by the eager step, which rewrites the
+// whole state every step (measured ~10% faster per eager step).  The DeltaLog
+// merge keeps the default policy: the hint sped up back-to-back merges but not
+// a merge cycle, whose appends otherwise absorb the write-back.
+__device__ __forceinline__ void buf_st4_stream(rsrc_t r, unsigned off, unsigned soff, float4 v)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, soff, kNonTemporal);
+}
 __device__ __forceinline__ float buf_ldf(rsrc_t r, unsigned off)
 {
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
@@ -856,8 +864,12 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
             }
         }
 #pragma unroll
-        for (int p = 0; p < P; ++p)
-            buf_st4(tile_r, xoff, p * RPP * DV * 4, x[p]);
+        for (int p = 0; p < P; ++p) {
+            if (MODE == EAGER)
+                buf_st4_stream(tile_r, xoff, p * RPP * DV * 4, x[p]);
+            else
+                buf_st4(tile_r, xoff, p * RPP * DV * 4, x[p]);
+        }
     }
 }
 
