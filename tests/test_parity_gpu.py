@@ -400,3 +400,39 @@ def test_full_size_graph_replay(orc, wid):
     print(f"[w{wid} full-size graph replay] worst o={worst_o:.2e} S={worst_S:.2e}", flush=True)
     st.close()
     assert worst_o < FP32_TOL and worst_S < FP32_TOL
+
+
+@needs_gpu
+def test_largest_state_the_abi_accepts(orc):
+    """The largest state below the 2^31-element limit at d=128: B*H = 131071
+    slot-heads (8 GiB of fp32 state), GDN bf16, M=2, three steps (a merge and a
+    pending log).  The base is zero except on 48 sampled slot-heads (first and
+    last included), whose seeded initial states and every output are checked
+    against the oracle, with the base after the final forced merge."""
+    import recurrent_state_update_amd as rsu
+    B, H, d, M = 131071, 1, 128, 2
+    assert B * H * d * d < 2**31 and (B + 1) * H * d * d >= 2**31
+    w = synth.Workload(19, "gdn", B, H, d, d, M, 3, "bf16")
+    idx = sample_slot_heads(B * H, 48, seed=19)
+    X0_rows = synth.initial(w.with_(B=len(idx)))[0].reshape(len(idx), d, d)  # seeded rows for the sample
+    base = torch.zeros(B, H, d, d, device="cuda")
+    sel = torch.from_numpy(idx).cuda()
+    base.view(B * H, d, d)[sel] = torch.from_numpy(X0_rows).cuda()
+    st = rsu.DeltaLogState("gdn", B, H, d, d, M, dtype=torch.bfloat16, base=base)
+    X = X0_rows.astype(np.float64)[None].copy()
+    worst_o = 0.0
+    for t in range(3):
+        s = synth.step(w, t)
+        d_ = {k_: dev(v_, torch.bfloat16 if k_ in ("q", "k", "v") else torch.float32) for k_, v_ in s.items()}
+        o = st.step(d_["q"], d_["k"], d_["v"], d_["beta"], d_["ld"])
+        sub = synth.subset(s, idx)
+        o_ref = orc.eager_step("gdn", X, sub["q"], sub["k"], sub["v"], sub["beta"], sub["ld"])
+        worst_o = max(worst_o, rel(o.view(B * H, d)[sel].cpu().numpy(), o_ref[0]))
+        del d_, o
+    st.merge()
+    worst_S = rel(base.view(B * H, d, d)[sel].cpu().numpy(), X[0])
+    print(f"[largest state] worst o={worst_o:.2e} S={worst_S:.2e}", flush=True)
+    st.close()
+    del base
+    torch.cuda.empty_cache()
+    assert worst_o < FP32_TOL and worst_S < FP32_TOL
