@@ -436,3 +436,58 @@ def test_largest_state_the_abi_accepts(orc):
     del base
     torch.cuda.empty_cache()
     assert worst_o < FP32_TOL and worst_S < FP32_TOL
+
+
+@needs_gpu
+@pytest.mark.parametrize("op", ["gdn", "kda", "rwkv6"])
+@pytest.mark.parametrize("shape", [(16, 16), (32, 128), (128, 32), (64, 64), (128, 128)])
+@pytest.mark.parametrize("path", ["fused", "staged", "eager"])
+def test_fp32_inputs(orc, op, shape, path):
+    """fp32 q/k/v (the kernels read whole 32-bit elements instead of picking
+    bf16 halves, and the RWKV6 b-log is fp32): every operator, square and
+    lopsided shapes, both DeltaLog paths and the eager kernel; M=3, 7 steps
+    (two merges and a pending log), then a forced merge."""
+    dk, dv = shape
+    w = synth.Workload(20, op, 2, 3, dk, dv, 3, 7, "f32")
+    run = ParityRun(w, eager=path == "eager", orc=orc)
+    for _ in range(7):
+        run.step(staged=path == "staged")
+    if path != "eager":
+        run.merge()
+    _report(run, f"fp32 {op} dk={dk} dv={dv} {path}")
+    run.close()
+
+
+@needs_gpu
+@pytest.mark.parametrize("op", ["gdn", "kda", "rwkv6"])
+def test_fp32_inputs_per_slot(orc, op):
+    """fp32 inputs on a handle with per-slot logs: two requests admitted late
+    with fresh seeded states, outputs every step and all bases after the
+    final merge."""
+    import recurrent_state_update_amd as rsu
+    B, H, M = 4, 2, 4
+    w = synth.Workload(21, op, B, H, 64, 64, M, 2 * M + 3, "f32")
+    X0, u = synth.initial(w)
+    st = rsu.DeltaLogState(op, B, H, 64, 64, M, dtype=torch.float32, base=dev(X0), u=dev(u))
+    st.enable_slots()
+    X = X0.reshape(B * H, 64, 64).astype(np.float64)[None].copy()
+    u_sub = None if u is None else u[np.arange(B * H) % H].astype(np.float64)
+    worst = 0.0
+    for t in range(w.steps):
+        if t in (1, 3):
+            b = t  # a new request in slot 1, then slot 3, from a fresh seeded state
+            new = synth.initial(w.with_(wid=2000 + t))[0][b]
+            st.base[b].copy_(dev(new))
+            st.admit(b)
+            X[0, b * H:(b + 1) * H] = new.astype(np.float64)
+        s = synth.step(w, t)
+        d_ = {k_: dev(v_) for k_, v_ in s.items()}
+        o = st.step(d_["q"], d_["k"], d_["v"], d_["beta"], d_["ld"])
+        sub = synth.subset(s, np.arange(B * H))
+        o_ref = orc.eager_step(op, X, sub["q"], sub["k"], sub["v"], sub["beta"], sub["ld"], u_sub)
+        worst = max(worst, rel(o.reshape(B * H, 64).cpu().numpy(), o_ref[0]))
+    st.merge()
+    worst_S = rel(st.base.reshape(B * H, 64, 64).cpu().numpy(), X[0])
+    st.close()
+    print(f"[fp32 per-slot {op}] worst o={worst:.2e} S={worst_S:.2e}", flush=True)
+    assert worst < FP32_TOL and worst_S < FP32_TOL
