@@ -170,7 +170,8 @@ def run_deltalog(w, inp, sts, K: int, W: int, instrument: bool, path: str = "fus
     torch.cuda.synchronize()
     t0.record(stream)
     for i in range(K):
-        ns.append(sts[(W + i) % R].log_len)
+        if instrument:
+            ns.append(sts[(W + i) % R].log_len)
         one(W + i, evs[i] if instrument else None)
     t1.record(stream)
     torch.cuda.synchronize()
@@ -188,21 +189,19 @@ def run_deltalog(w, inp, sts, K: int, W: int, instrument: bool, path: str = "fus
 
 
 def graph_len(period: int, pool: int, K: int) -> int:
-    """Launches per captured graph: a whole number of schedule periods that
-    also walks the whole input pool when that divides K, else one period."""
+    """Launches per captured graph: whole schedule periods that also walk the
+    whole input pool when that fits K whole times, else one period."""
     import math
     full = period * pool // math.gcd(period, pool)
-    if K % full == 0:
-        return full
-    if K % period == 0:
-        return period
-    raise SystemExit(f"--steps {K} must be a multiple of {period} (states x merge interval)")
+    return full if K % full == 0 else period
 
 
 def time_graph(launch, G: int, K: int, W: int) -> float:
-    """Capture launch(0..G-1) as one HIP graph, replay it ceil(W/G) times
-    untimed, then K/G times between two HIP events on the replay stream.
-    Returns ms per launch."""
+    """Capture launch(0..G-1) as one HIP graph and replay it ceil(W/G) times
+    untimed.  Then, between two HIP events on the replay stream, replay it
+    K // G times and issue the remaining K % G launches directly (continuing
+    the same sequence), so that exactly K launches are timed.  Returns ms per
+    launch."""
     import torch
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
@@ -214,11 +213,14 @@ def time_graph(launch, G: int, K: int, W: int) -> float:
         g.replay()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record(stream)
     for _ in range(K // G):
         g.replay()
+    for i in range(K % G):
+        launch(i, sp)
     t1.record(stream)
     torch.cuda.synchronize()
     return t0.elapsed_time(t1) / K
@@ -227,7 +229,9 @@ def time_graph(launch, G: int, K: int, W: int) -> float:
 def run_graph(w, inp, sts, K: int, W: int):
     """DeltaLog steps replayed from a HIP graph: G launches (state i % R,
     inputs i % pool; whole merge cycles of every state) captured once and
-    replayed.  Every state starts from an empty log.  Returns ms per step."""
+    replayed, any remainder of K launched directly.  Every state starts from
+    an empty log.  Returns (ms per step, mean algorithmic bytes per launch of
+    the K timed steps)."""
     import recurrent_state_update_amd as rsu
     import torch
     R = len(sts)
@@ -241,9 +245,18 @@ def run_graph(w, inp, sts, K: int, W: int):
     def launch(i, sp):
         q, k, v, beta, ld = ptrs[i % pool]
         if rsu._lib.dl_decode_step(hs[i % R], q, k, v, beta, ld, o.data_ptr(), sp) != 0:
-            raise RuntimeError("dl_decode_step failed under capture")
+            raise RuntimeError("dl_decode_step failed")
 
-    return time_graph(launch, graph_len(R * w.M, pool, K), K, W)
+    G = graph_len(R * w.M, pool, K)
+    ms = time_graph(launch, G, K, W)
+    # bytes: whole cycles at the cycle mean; the remainder launch i steps
+    # state i % R at log length (i // R) mod M
+    rem = K % G
+    tot = (K - rem) * cycle_launch_bytes(w)
+    for i in range(rem):
+        n = (i // R) % w.M
+        tot += step_launch_bytes(w, n, n + 1 == w.M)
+    return ms, tot / K
 
 
 def run_eager_graph(w, inp, bases, u_dev, K: int, W: int):
@@ -263,7 +276,7 @@ def run_eager_graph(w, inp, bases, u_dev, K: int, W: int):
         q, k, v, beta, ld = ptrs[i % pool]
         if rsu._lib.dl_eager_step(opi, w.B, w.H, w.dk, w.dv, dti, bptr[i % R], q, k, v, beta, ld,
                                   uptr, o.data_ptr(), sp) != 0:
-            raise RuntimeError("dl_eager_step failed under capture")
+            raise RuntimeError("dl_eager_step failed")
 
     return time_graph(launch, graph_len(R, pool, K), K, W)
 
@@ -436,8 +449,7 @@ def bench_workload(w, K, W, R, pool, with_eager=True, with_staged=True, quick=Fa
     inp = stage_inputs(w, pool, dt)
     sts, base0, u_dev = make_states(w, R, dt)
     res = {}
-    gms = run_graph(w, inp, sts, K, W)
-    per_launch = cycle_launch_bytes(w)
+    gms, per_launch = run_graph(w, inp, sts, K, W)
     res["wall_ms"] = gms * K
     res["value"] = w.BH / (gms * 1e-3)
     achieved = per_launch / (gms * 1e-3) / 1e9
@@ -453,12 +465,21 @@ def bench_workload(w, K, W, R, pool, with_eager=True, with_staged=True, quick=Fa
     for st in sts:
         st.merge()
     wall, _, _ = run_deltalog(w, inp, sts, K, W, instrument=False, path="fused")
+    # the direct loop steps state i % R from an empty log, W of them untimed
+    cnt = [0] * R
+    direct_tot = 0
+    for i in range(W + K):
+        n = cnt[i % R] % w.M
+        if i >= W:
+            direct_tot += step_launch_bytes(w, n, n + 1 == w.M)
+        cnt[i % R] += 1
+    direct_bytes = direct_tot / K
     if quick:
         launches = []
     else:
         _, launches, _ = run_deltalog(w, inp, sts, K, W, instrument=True, path="fused")
     res["direct_launch"] = dict(value=round(w.BH * K / (wall * 1e-3), 1), ms_per_step=round(wall / K, 5),
-                                achieved_GBs=round(per_launch / (wall / K * 1e-3) / 1e9, 1))
+                                achieved_GBs=round(direct_bytes / (wall / K * 1e-3) / 1e9, 1))
     app = [x[0] for x in launches if not x[2]]
     mer = [x[0] for x in launches if x[2]]
     res["roofline"]["event_bracketed_us"] = dict(append=round(1e3 * sum(app) / max(len(app), 1), 2),
