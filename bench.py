@@ -408,7 +408,8 @@ def cpu_baseline(w, budget_s=(8.0, 5.0), pool: int = 32):
     orc.set_threads(threads)
     v, done, spent = out[threads]
     v1, done1, spent1 = out[1]
-    return dict(value=round(v, 1), unit="(token·head)/s", cores=threads, kind="oracle",
+    return dict(value=round(v, 1), unit="(token·head)/s", cores=threads, nproc=os.cpu_count(),
+                kind="oracle",
                 sample=f"fp64 eager oracle over all {w.BH} slot-heads of {w.describe()}, cycling its "
                        f"first {len(steps)} steps' inputs: {done} steps on {threads} threads in "
                        f"{spent:.1f} s; on 1 thread {round(v1, 1)} (token·head)/s ({done1} steps in "
