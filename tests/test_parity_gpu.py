@@ -491,3 +491,34 @@ def test_fp32_inputs_per_slot(orc, op):
     st.close()
     print(f"[fp32 per-slot {op}] worst o={worst:.2e} S={worst_S:.2e}", flush=True)
     assert worst < FP32_TOL and worst_S < FP32_TOL
+
+
+@needs_gpu
+@pytest.mark.parametrize("op", ["gdn", "kda", "rwkv6"])
+def test_runs_are_bit_identical(op):
+    """The kernels use no atomics and a fixed reduction order, so two runs of
+    the same steps on fresh states give bit-identical outputs and bases, for
+    lockstep and per-slot handles alike."""
+    import recurrent_state_update_amd as rsu
+    w = synth.Workload(22, op, 4, 8, 128, 128, 4, 11, "bf16")
+    X0, u = synth.initial(w)
+    dt = in_dtype(w)
+    steps = [{k_: dev(v_, dt if k_ in ("q", "k", "v") else torch.float32) for k_, v_ in synth.step(w, t).items()}
+             for t in range(w.steps)]
+    for slots in (False, True):
+        runs = []
+        for _ in range(2):
+            st = rsu.DeltaLogState(op, w.B, w.H, w.dk, w.dv, w.M, dtype=dt, base=dev(X0), u=dev(u))
+            if slots:
+                st.enable_slots()
+            outs = []
+            for t, s in enumerate(steps):
+                if slots and t == 2:
+                    st.admit(1)
+                outs.append(st.step(s["q"], s["k"], s["v"], s["beta"], s["ld"]).clone())
+            st.merge()
+            runs.append((outs, st.base.clone()))
+            st.close()
+        (oa, ba), (ob, bb) = runs
+        assert all(torch.equal(x, y) for x, y in zip(oa, ob)), (op, slots)
+        assert torch.equal(ba, bb), (op, slots)
