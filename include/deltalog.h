@@ -36,11 +36,12 @@
  *   log_decay      GDN [B,H] fp32; KDA, RWKV6 [B,H,d_k] fp32 (natural log, <= 0)
  *   u              RWKV6 bonus [H,d_k] fp32 (NULL for GDN, KDA)
  *   o              [B,H,d_v] fp32, 16-byte aligned
- *   workspace      dl_workspace_bytes() bytes, 256-byte aligned; holds the log
- *                  and per-step coefficients; contents need no initialisation
+ *   workspace      dl_workspace_bytes() bytes, 256-byte aligned; holds the log,
+ *                  the two-stage path's per-step coefficients and the per-slot
+ *                  log phases; contents need no initialisation
  * Supported shapes: d_k, d_v in {16, 32, 64, 128}; 1 <= M <= 32; B, H >= 1
  * with B*H*d_k*d_v < 2^31.  All B slots step in lockstep (one shared log
- * length).
+ * length) unless per-slot logs are enabled (see the end of this file).
  *
  * Errors and ownership.  Every call returns a dl_status and never aborts or
  * throws.  Arguments are validated on the host before any HIP call (so bad
