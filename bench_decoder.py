@@ -69,7 +69,10 @@ class SyntheticDecoder:
         for l in range(ds.L):
             if weights_from is None:
                 p = synth.decoder_layer(ds, l)
-                lay = {k: torch.from_numpy(p[k]).cuda().to(wdtype) for k in ("W_in", "W_o", "W_gu", "W_dn")}
+                # kept as [out, in] (the nn.Linear layout, for which the
+                # library GEMM picks a better kernel at decode batch sizes)
+                lay = {k: torch.from_numpy(p[k]).cuda().to(wdtype).t().contiguous()
+                       for k in ("W_in", "W_o", "W_gu", "W_dn")}
                 lay["u"] = None if p["u"] is None else torch.from_numpy(p["u"]).cuda()
                 lay["X0"] = p["X0"]
             else:
@@ -94,7 +97,7 @@ class SyntheticDecoder:
         ds = self.ds
         B, H = ds.B, ds.H
         h = F.rms_norm(x, (ds.hidden,), eps=EPS).to(self.wd)
-        p = (h @ lay["W_in"]).float()
+        p = F.linear(h, lay["W_in"]).float()
         q, k, v, zb, zd = torch.split(p, ds.proj_split, dim=1)
         q = q.reshape(B, H, ds.dk)
         k = k.reshape(B, H, ds.dk)
@@ -120,10 +123,10 @@ class SyntheticDecoder:
         ds = self.ds
         for lay in self.layers:
             o = self.state_step(lay, *self.layer_inputs(x, lay))
-            x = x + (o.reshape(ds.B, ds.H * ds.dv).to(self.wd) @ lay["W_o"]).float()
-            gu = (F.rms_norm(x, (ds.hidden,), eps=EPS).to(self.wd) @ lay["W_gu"]).float()
+            x = x + F.linear(o.reshape(ds.B, ds.H * ds.dv).to(self.wd), lay["W_o"]).float()
+            gu = F.linear(F.rms_norm(x, (ds.hidden,), eps=EPS).to(self.wd), lay["W_gu"]).float()
             g, u = gu.split(ds.ffn, dim=1)
-            x = x + ((F.silu(g) * u).to(self.wd) @ lay["W_dn"]).float()
+            x = x + F.linear((F.silu(g) * u).to(self.wd), lay["W_dn"]).float()
         return x, F.rms_norm(x, (ds.hidden,), eps=EPS)
 
     def capture_cycle(self, x_static):
