@@ -522,3 +522,42 @@ def test_runs_are_bit_identical(op):
         (oa, ba), (ob, bb) = runs
         assert all(torch.equal(x, y) for x, y in zip(oa, ob)), (op, slots)
         assert torch.equal(ba, bb), (op, slots)
+
+
+@needs_gpu
+@pytest.mark.parametrize("op", ["gdn", "kda"])
+def test_large_batch_long_run(orc, op):
+    """The large-batch configuration at its full length: B=256 H=32 d=128
+    (512 MiB state), M=8, all 1024 decode steps (128 merges), inputs cycling
+    a staged pool of 64 steps as the benchmark does.  32 sampled slot-heads:
+    every output, and the base after every merge, against the oracle (no
+    drift over the run)."""
+    import recurrent_state_update_amd as rsu
+    w = synth.sweep_workload(op, 8, steps=1024)
+    pool = 64
+    idx = sample_slot_heads(w.BH, 32, seed=41)
+    sel = torch.from_numpy(idx).cuda()
+    X0, u = synth.initial(w)
+    dt = in_dtype(w)
+    base = dev(X0)
+    st = rsu.DeltaLogState(op, w.B, w.H, w.dk, w.dv, w.M, dtype=dt, base=base, u=dev(u))
+    staged, subs = [], []
+    for s_ in range(pool):
+        s = synth.step(w, s_)
+        staged.append({k_: dev(v_, dt if k_ in ("q", "k", "v") else torch.float32) for k_, v_ in s.items()})
+        subs.append(synth.subset(s, idx))
+    X = X0.reshape(w.BH, w.dk, w.dv)[idx].astype(np.float64)[None].copy()
+    worst_o = worst_S = 0.0
+    merges = 0
+    for t in range(w.steps):
+        d_, sub = staged[t % pool], subs[t % pool]
+        o = st.step(d_["q"], d_["k"], d_["v"], d_["beta"], d_["ld"])
+        o_ref = orc.eager_step(op, X, sub["q"], sub["k"], sub["v"], sub["beta"], sub["ld"])
+        worst_o = max(worst_o, rel(o.reshape(w.BH, w.dv)[sel].cpu().numpy(), o_ref[0]))
+        if st.log_len == 0:
+            merges += 1
+            worst_S = max(worst_S, rel(base.reshape(w.BH, w.dk, w.dv)[sel].cpu().numpy(), X[0]))
+    print(f"[{op} B=256 M=8 1024 steps] worst o={worst_o:.2e} S={worst_S:.2e} merges {merges}", flush=True)
+    st.close()
+    assert merges == 128
+    assert worst_o < FP32_TOL and worst_S < FP32_TOL
