@@ -284,8 +284,9 @@ def run_eager_graph(w, inp, bases, u_dev, K: int, W: int):
 def run_per_slot(w, inp, R: int, K: int, W: int):
     """Continuous batching: R fresh states with per-slot logs, slot b admitted
     at step b % M, so in steady state every launch merges the B/M slots whose
-    logs are full and appends for the rest.  Returns wall ms of K launches and
-    the algorithmic bytes they move."""
+    logs are full and appends for the rest.  Then the odd slots are released
+    (half-occupied batch) and the same K launches are timed again.  Returns
+    (wall ms, algorithmic bytes) of K launches, full and half occupied."""
     import torch
     import synth
     import recurrent_state_update_amd as rsu
@@ -327,17 +328,27 @@ def run_per_slot(w, inp, R: int, K: int, W: int):
     torch.cuda.synchronize()
     cyc = min(K, R * w.M)
     nbytes = nbytes * K / cyc
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for i in range(K):
+    def timed():
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for i in range(K):
+            one(i)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1)
+
+    wall = timed()
+    for st in sts:  # half of the requests finish: their slots are released
+        for b in range(1, w.B, 2):
+            st.release(b)
+    half_bytes = nbytes * (w.B // 2 + w.B % 2) / w.B  # the slots b % M are spread evenly
+    for i in range(W):
         one(i)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    wall = t0.elapsed_time(t1)
+    wall_half = timed()
     for st in sts:
         st.close()
-    return wall, nbytes
+    return wall, nbytes, wall_half, half_bytes
 
 
 def run_eager(w, inp, bases, u_dev, K: int, W: int, instrument: bool):
@@ -489,11 +500,13 @@ def bench_workload(w, K, W, R, pool, with_eager=True, with_staged=True, quick=Fa
         one, _, _ = run_deltalog(w, inp, sts[:1], K, W, instrument=False)
         res["single_state_value"] = round(w.BH * K / (one * 1e-3), 1)
     if not quick:
-        pw, pbytes = run_per_slot(w, inp, R, K, W)
+        pw, pbytes, hw, hbytes = run_per_slot(w, inp, R, K, W)
         res["per_slot"] = dict(value=round(w.BH * K / (pw * 1e-3), 1), ms_per_step=round(pw / K, 5),
                                achieved_GBs=round(pbytes / (pw * 1e-3) / 1e9, 1),
                                frac=round(pbytes / (pw * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                               launch="direct")
+                               launch="direct",
+                               half_released=dict(ms_per_step=round(hw / K, 5),
+                                                  achieved_GBs=round(hbytes / (hw * 1e-3) / 1e9, 1)))
     if with_staged:
         sw, _, _ = run_deltalog(w, inp, sts, K, W, instrument=False, path="staged")
         _, sl, sp = run_deltalog(w, inp, sts, K, W, instrument=True, path="staged")

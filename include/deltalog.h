@@ -165,18 +165,25 @@ int dl_suggest_merge_interval(int B, int H, int d_k, int d_v, dl_op op, dl_dtype
  * dl_state_reset return DL_E_STATE. */
 dl_status dl_state_enable_slots(dl_state *s, void *stream);
 
-/* Admit a new request into `slot`: drop the slot's pending log without
- * folding it.  The caller writes the request's initial state into the slot's
+/* Admit a new request into `slot` (also one released before): drop the
+ * slot's pending log without folding it.  The caller writes the request's initial state into the slot's
  * rows of `base` ([slot, 0..H)) before the next step (stream-ordered). */
 dl_status dl_slot_admit(dl_state *s, int slot, void *stream);
 
 /* Fold the pending entries of one slot into its rows of `base` (which then
  * hold that slot's logical state) and empty its log.  No-op when the slot's
- * log is empty.  Use before reading a finished request's state. */
+ * log is empty or the slot is released.  Use before reading a finished
+ * request's state. */
 dl_status dl_slot_merge(dl_state *s, int slot, void *stream);
 
-/* Pending entries of one slot (the shared count on a lockstep handle), -1 for
- * a bad handle or slot. */
+/* Release `slot` (its request finished; merge it first to keep its state):
+ * until the next dl_slot_admit of this slot, decode steps and merges skip
+ * it entirely (no reads, no writes; its rows of `base`, its outputs in `o`
+ * and its log are left untouched), so empty slots cost no memory traffic. */
+dl_status dl_slot_release(dl_state *s, int slot, void *stream);
+
+/* Pending entries of one slot (the shared count on a lockstep handle; 0 for
+ * a released slot), -1 for a bad handle or slot. */
 int dl_slot_log_len(const dl_state *s, int slot);
 
 /* Static description of a status code. */

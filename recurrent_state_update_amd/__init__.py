@@ -30,7 +30,8 @@ STATUS = {0: "DL_OK", 1: "DL_E_INVALID", 2: "DL_E_SHAPE", 3: "DL_E_ALIGN", 4: "D
 EXPORTS = ("dl_workspace_bytes", "dl_state_create", "dl_decode_step", "dl_replay_prep",
            "dl_append_decode", "dl_merge", "dl_state_reset", "dl_log_len", "dl_set_log_len",
            "dl_state_destroy", "dl_eager_step", "dl_status_string", "dl_suggest_merge_interval",
-           "dl_state_enable_slots", "dl_slot_admit", "dl_slot_merge", "dl_slot_log_len")
+           "dl_state_enable_slots", "dl_slot_admit", "dl_slot_merge", "dl_slot_log_len",
+           "dl_slot_release")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run `python recurrent_state_update_amd/_build.py` "
@@ -56,6 +57,7 @@ _SIG = {
     "dl_slot_admit": ([_p, _i, _p], _i),
     "dl_slot_merge": ([_p, _i, _p], _i),
     "dl_slot_log_len": ([_p, _i], _i),
+    "dl_slot_release": ([_p, _i, _p], _i),
 }
 for _name, (_args, _res) in _SIG.items():
     _f = getattr(_lib, _name)
@@ -167,6 +169,10 @@ def dl_slot_log_len(s, slot) -> int:
     return _lib.dl_slot_log_len(s, slot)
 
 
+def dl_slot_release(s, slot, stream=None):
+    return _lib.dl_slot_release(s, slot, _stream(stream))
+
+
 def dl_status_string(st) -> str:
     return _lib.dl_status_string(st).decode()
 
@@ -264,6 +270,12 @@ class DeltaLogState:
 
     def merge_slot(self, slot: int, stream=None):
         _check(dl_slot_merge(self._h, slot, stream), "dl_slot_merge")
+
+    def release(self, slot: int, stream=None):
+        """The request in ``slot`` finished: later steps and merges skip the
+        slot (no traffic) until it is admitted again.  Merge it first to keep
+        its state."""
+        _check(dl_slot_release(self._h, slot, stream), "dl_slot_release")
 
     def slot_log_len(self, slot: int) -> int:
         return dl_slot_log_len(self._h, slot)

@@ -28,7 +28,8 @@ struct dl_state {
     int n;        // pending log entries (lockstep schedule)
     bool prepped; // ReplayPrep ran for the step in progress
     // per-slot schedule (continuous batching): slot b holds (tm - t0[b]) mod M
-    // entries; t0 is mirrored here and in the workspace
+    // entries, or is released (no request) when t0[b] < 0; t0 is mirrored
+    // here and in the workspace
     bool per_slot;
     int tm;       // steps taken, mod M
     int *t0;      // host mirror [B]
@@ -55,21 +56,22 @@ Layout workspace_layout(long B, long H, int dk, int dv, int M, int op, int dtype
     return l;
 }
 
-// Set the phase of one slot (or of all when slot < 0).  A kernel rather than
-// a memset so that calls stay capturable into HIP graphs.
-__global__ void slot_phase_kernel(int *t0, int B, int slot, int value)
+// Set the phase of one slot (or of all when slot < 0, skipping released
+// slots when active_only).  A kernel rather than a memset so that calls stay
+// capturable into HIP graphs.
+__global__ void slot_phase_kernel(int *t0, int B, int slot, int value, int active_only)
 {
     const int b = blockIdx.x * blockDim.x + threadIdx.x;
-    if (b < B && (slot < 0 || b == slot))
+    if (b < B && (slot < 0 || b == slot) && !(active_only && t0[b] < 0))
         t0[b] = value;
 }
 
-hipError_t launch_slot_phase(int *t0, int B, int slot, int value, hipStream_t st)
+hipError_t launch_slot_phase(int *t0, int B, int slot, int value, bool active_only, hipStream_t st)
 {
     const int blocks = slot >= 0 ? 1 : (B + 255) / 256;
     const int first = slot >= 0 ? slot : 0;
     hipLaunchKernelGGL(slot_phase_kernel, dim3(blocks), dim3(slot >= 0 ? 1 : 256), 0, st,
-                       t0 + first, slot >= 0 ? 1 : B, slot >= 0 ? 0 : -1, value);
+                       t0 + first, slot >= 0 ? 1 : B, slot >= 0 ? 0 : -1, value, active_only ? 1 : 0);
     return hipGetLastError();
 }
 
@@ -292,10 +294,11 @@ dl_status dl_merge(dl_state *s, void *stream)
         dl::StepArgs a = make_args(s);
         const hipStream_t st = static_cast<hipStream_t>(stream);
         if (launch_step(s->op, s->dtype, s->dk, s->dv, dl::SFOLD, a, st) != hipSuccess ||
-            dl::launch_slot_phase(slot_phases(s), s->B, -1, s->tm, st) != hipSuccess)
+            dl::launch_slot_phase(slot_phases(s), s->B, -1, s->tm, true, st) != hipSuccess)
             return DL_E_HIP;
         for (int b = 0; b < s->B; ++b)
-            s->t0[b] = s->tm;
+            if (s->t0[b] >= 0)
+                s->t0[b] = s->tm;
         return DL_OK;
     }
     if (s->n == 0)
@@ -347,7 +350,8 @@ dl_status dl_state_enable_slots(dl_state *s, void *stream)
         return DL_E_INVALID;
     if (s->prepped || s->n != 0 || s->per_slot)
         return DL_E_STATE;
-    if (dl::launch_slot_phase(slot_phases(s), s->B, -1, 0, static_cast<hipStream_t>(stream)) != hipSuccess)
+    if (dl::launch_slot_phase(slot_phases(s), s->B, -1, 0, false, static_cast<hipStream_t>(stream)) !=
+        hipSuccess)
         return DL_E_HIP;
     s->per_slot = true;
     s->tm = 0;
@@ -362,10 +366,23 @@ dl_status dl_slot_admit(dl_state *s, int slot, void *stream)
         return DL_E_INVALID;
     if (!s->per_slot)
         return DL_E_STATE;
-    if (dl::launch_slot_phase(slot_phases(s), s->B, slot, s->tm, static_cast<hipStream_t>(stream)) !=
+    if (dl::launch_slot_phase(slot_phases(s), s->B, slot, s->tm, false, static_cast<hipStream_t>(stream)) !=
         hipSuccess)
         return DL_E_HIP;
     s->t0[slot] = s->tm;
+    return DL_OK;
+}
+
+dl_status dl_slot_release(dl_state *s, int slot, void *stream)
+{
+    if (!s || slot < 0 || slot >= s->B)
+        return DL_E_INVALID;
+    if (!s->per_slot)
+        return DL_E_STATE;
+    if (dl::launch_slot_phase(slot_phases(s), s->B, slot, -1, false, static_cast<hipStream_t>(stream)) !=
+        hipSuccess)
+        return DL_E_HIP;
+    s->t0[slot] = -1;
     return DL_OK;
 }
 
@@ -375,13 +392,13 @@ dl_status dl_slot_merge(dl_state *s, int slot, void *stream)
         return DL_E_INVALID;
     if (!s->per_slot)
         return DL_E_STATE;
-    if (dl_slot_log_len(s, slot) == 0)
+    if (dl_slot_log_len(s, slot) == 0) // nothing pending, or a released slot
         return DL_OK;
     dl::StepArgs a = make_args(s);
     a.slot = slot;
     const hipStream_t st = static_cast<hipStream_t>(stream);
     if (launch_step(s->op, s->dtype, s->dk, s->dv, dl::SFOLD, a, st) != hipSuccess ||
-        dl::launch_slot_phase(slot_phases(s), s->B, slot, s->tm, st) != hipSuccess)
+        dl::launch_slot_phase(slot_phases(s), s->B, slot, s->tm, false, st) != hipSuccess)
         return DL_E_HIP;
     s->t0[slot] = s->tm;
     return DL_OK;
@@ -393,6 +410,8 @@ int dl_slot_log_len(const dl_state *s, int slot)
         return -1;
     if (!s->per_slot)
         return s->n;
+    if (s->t0[slot] < 0) // released: no request, nothing pending
+        return 0;
     return (s->tm - s->t0[slot] + s->M) % s->M;
 }
 

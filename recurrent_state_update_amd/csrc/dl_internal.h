@@ -68,7 +68,9 @@ struct StepArgs {
 hipError_t launch_prep_gdn(int dtype, int dk, const StepArgs &a, hipStream_t st);
 hipError_t launch_prep_kda(int dtype, int dk, const StepArgs &a, hipStream_t st);
 hipError_t launch_prep_rwkv6(int dtype, int dk, const StepArgs &a, hipStream_t st);
-hipError_t launch_slot_phase(int *t0, int B, int slot, int value, hipStream_t st);
+// Set slot phases: one slot (slot >= 0), or all slots (slot < 0; with
+// active_only, only those not released).  A kernel, so calls stay capturable.
+hipError_t launch_slot_phase(int *t0, int B, int slot, int value, bool active_only, hipStream_t st);
 hipError_t launch_step_gdn(int dtype, int dk, int dv, int mode, const StepArgs &a, hipStream_t st);
 hipError_t launch_step_kda(int dtype, int dk, int dv, int mode, const StepArgs &a, hipStream_t st);
 hipError_t launch_step_rwkv6(int dtype, int dk, int dv, int mode, const StepArgs &a, hipStream_t st);

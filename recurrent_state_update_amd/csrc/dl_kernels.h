@@ -420,8 +420,13 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
     const int tile = blockIdx.x % NTILE;
     const int col = tile * T + 4 * c4;
     const int M = a.M;
-    // log length: shared by all slots, or this slot's own (wave-uniform)
-    const int n = SLOTS ? (a.tm - a.t0[sh / a.H] + M) % M : a.n;
+    // log length: shared by all slots, or this slot's own (wave-uniform); a
+    // released slot (phase < 0) holds no request, so its workgroups leave
+    // before any load
+    const int phase = SLOTS ? a.t0[sh / a.H] : 0;
+    if (SLOTS && phase < 0)
+        return;
+    const int n = SLOTS ? (a.tm - phase + M) % M : a.n;
     if (MODE == SFOLD && n == 0)
         return; // nothing pending for this slot (whole workgroup leaves)
     const bool merging = MODE == MERGE || MODE == FMERGE || (MODE == SSTEP && n == M - 1);

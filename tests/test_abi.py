@@ -173,6 +173,8 @@ def test_per_slot_calls_validate_before_any_launch():
         assert rsu.dl_state_enable_slots(h, s) == STATE  # needs an empty log
         assert rsu.dl_slot_log_len(h, 3) == 2
         assert rsu.dl_state_enable_slots(None, s) == INVALID
+        assert rsu.dl_slot_release(h, 0, s) == STATE     # lockstep handle
+        assert rsu.dl_slot_release(h, 4, s) == INVALID and rsu.dl_slot_release(None, 0, s) == INVALID
     finally:
         rsu.dl_state_destroy(h)
 

@@ -561,3 +561,59 @@ def test_large_batch_long_run(orc, op):
     st.close()
     assert merges == 128
     assert worst_o < FP32_TOL and worst_S < FP32_TOL
+
+
+@needs_gpu
+@pytest.mark.parametrize("op", ["gdn", "rwkv6"])
+def test_released_slots_are_skipped(orc, op):
+    """A finished request is merged and its slot released: later steps and
+    merges leave that slot's base rows and outputs untouched (no traffic),
+    while the other slots keep matching the oracle; the slot is then admitted
+    again with a fresh state and matches the oracle from there."""
+    import recurrent_state_update_amd as rsu
+    B, H, M = 5, 2, 4
+    w = synth.Workload(23, op, B, H, 64, 64, M, 14, "bf16")
+    X0, u = synth.initial(w)
+    dt = in_dtype(w)
+    st = rsu.DeltaLogState(op, B, H, 64, 64, M, dtype=dt, base=dev(X0), u=dev(u))
+    st.enable_slots()
+    X = X0.reshape(B * H, 64, 64).astype(np.float64)[None].copy()
+    u_sub = None if u is None else u[np.arange(B * H) % H].astype(np.float64)
+    rows = lambda b: slice(b * H, (b + 1) * H)
+    o = torch.full((B, H, 64), float("nan"), device="cuda")
+    live = [True] * B
+    worst = 0.0
+    frozen = None
+    for t in range(w.steps):
+        if t == 5:   # slot 2 finishes: merge, keep its state, release
+            st.merge_slot(2)
+            st.release(2)
+            frozen = st.base[2].clone()
+            assert rel(frozen.cpu().numpy(), X[0, rows(2)]) < FP32_TOL
+            live[2] = False
+            o[2].fill_(float("nan"))
+            assert st.slot_log_len(2) == 0
+        if t == 10:  # a new request in slot 2
+            new = synth.initial(w.with_(wid=3000))[0][2]
+            st.base[2].copy_(dev(new))
+            st.admit(2)
+            X[0, rows(2)] = new.astype(np.float64)
+            live[2] = True
+        s = synth.step(w, t)
+        d_ = {k_: dev(v_, dt if k_ in ("q", "k", "v") else torch.float32) for k_, v_ in s.items()}
+        st.step(d_["q"], d_["k"], d_["v"], d_["beta"], d_["ld"], o=o)
+        sub = synth.subset(s, np.arange(B * H))
+        Xprev = X[0, rows(2)].copy()
+        o_ref = orc.eager_step(op, X, sub["q"], sub["k"], sub["v"], sub["beta"], sub["ld"], u_sub)
+        if not live[2]:
+            X[0, rows(2)] = Xprev  # the oracle leaves the released slot alone too
+            assert torch.isnan(o[2]).all()
+            assert torch.equal(st.base[2], frozen)
+        for b in range(B):
+            if live[b]:
+                worst = max(worst, rel(o[b].reshape(H, 64).cpu().numpy(), o_ref[0, rows(b)]))
+    st.merge()
+    worst_S = max(rel(st.base[b].cpu().numpy(), X[0, rows(b)]) for b in range(B))
+    st.close()
+    print(f"[{op} release] worst o={worst:.2e} S={worst_S:.2e}", flush=True)
+    assert worst < FP32_TOL and worst_S < FP32_TOL
