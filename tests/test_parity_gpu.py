@@ -617,3 +617,49 @@ def test_released_slots_are_skipped(orc, op):
     st.close()
     print(f"[{op} release] worst o={worst:.2e} S={worst_S:.2e}", flush=True)
     assert worst < FP32_TOL and worst_S < FP32_TOL
+
+
+@needs_gpu
+@pytest.mark.parametrize("op", ["gdn", "kda", "rwkv6"])
+def test_per_slot_long_logs(orc, op):
+    """Per-slot logs at the largest merge interval (M=32, d=128, two value
+    tiles): slots admitted at different steps hold logs of very different
+    lengths in one launch, so long-log workgroups (the second staging pass of
+    the log shard, one-entry-per-wave coefficients) run beside short-log and
+    merging ones.  Every output and each slot's base after its own merge."""
+    import recurrent_state_update_amd as rsu
+    B, H, M = 3, 2, 32
+    w = synth.Workload(25, op, B, H, 128, 128, M, 2 * M + 9, "bf16")
+    X0, u = synth.initial(w)
+    dt = in_dtype(w)
+    st = rsu.DeltaLogState(op, B, H, 128, 128, M, dtype=dt, base=dev(X0), u=dev(u))
+    st.enable_slots()
+    X = X0.reshape(B * H, 128, 128).astype(np.float64)[None].copy()
+    u_sub = None if u is None else u[np.arange(B * H) % H].astype(np.float64)
+    rows = lambda b: slice(b * H, (b + 1) * H)
+    admissions = {7: 1, 19: 2}
+    worst_o = worst_S = 0.0
+    merged = set()
+    for t in range(w.steps):
+        if t in admissions:
+            b = admissions[t]
+            new = synth.initial(w.with_(wid=4000 + t))[0][b]
+            st.base[b].copy_(dev(new))
+            st.admit(b)
+            X[0, rows(b)] = new.astype(np.float64)
+        s = synth.step(w, t)
+        d_ = {k_: dev(v_, dt if k_ in ("q", "k", "v") else torch.float32) for k_, v_ in s.items()}
+        o = st.step(d_["q"], d_["k"], d_["v"], d_["beta"], d_["ld"])
+        sub = synth.subset(s, np.arange(B * H))
+        o_ref = orc.eager_step(op, X, sub["q"], sub["k"], sub["v"], sub["beta"], sub["ld"], u_sub)
+        worst_o = max(worst_o, rel(o.reshape(B * H, 128).cpu().numpy(), o_ref[0]))
+        for b in range(B):
+            if st.slot_log_len(b) == 0:
+                merged.add(b)
+                worst_S = max(worst_S, rel(st.base[b].cpu().numpy(), X[0, rows(b)]))
+    st.merge()
+    worst_S = max(worst_S, max(rel(st.base[b].cpu().numpy(), X[0, rows(b)]) for b in range(B)))
+    st.close()
+    print(f"[{op} per-slot M=32] worst o={worst_o:.2e} S={worst_S:.2e} slots merged {sorted(merged)}", flush=True)
+    assert merged == {0, 1, 2}
+    assert worst_o < FP32_TOL and worst_S < FP32_TOL
