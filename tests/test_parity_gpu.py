@@ -663,3 +663,85 @@ def test_per_slot_long_logs(orc, op):
     print(f"[{op} per-slot M=32] worst o={worst_o:.2e} S={worst_S:.2e} slots merged {sorted(merged)}", flush=True)
     assert merged == {0, 1, 2}
     assert worst_o < FP32_TOL and worst_S < FP32_TOL
+
+
+@needs_gpu
+@pytest.mark.parametrize("op", ["gdn", "kda", "rwkv6"])
+def test_graph_capture_per_slot(orc, op):
+    """Per-slot logs under HIP graph capture: one merge cycle captured, then
+    replayed three times with fresh inputs; between replays a request is
+    admitted (new state written into its slot) and another released, outside
+    the graph.  Every replay matches a twin handle driven by direct launches
+    bit for bit, and the oracle on the live slots."""
+    import recurrent_state_update_amd as rsu
+    B, H, M = 4, 2, 4
+    w = synth.Workload(26, op, B, H, 64, 128, M, 3 * M, "bf16")
+    X0, u = synth.initial(w)
+    dt = in_dtype(w)
+    a = rsu.DeltaLogState(op, B, H, 64, 128, M, dtype=dt, base=dev(X0), u=dev(u))
+    b = rsu.DeltaLogState(op, B, H, 64, 128, M, dtype=dt, base=dev(X0), u=dev(u))
+    for st in (a, b):
+        st.enable_slots()
+    # stagger slot 3 before capture (both handles alike)
+    warm = [{k_: dev(v_, dt if k_ in ("q", "k", "v") else torch.float32) for k_, v_ in synth.step(w.with_(wid=27), t).items()}
+            for t in range(2)]
+    X = X0.reshape(B * H, 64, 128).astype(np.float64)[None].copy()
+    u_sub = None if u is None else u[np.arange(B * H) % H].astype(np.float64)
+    for t, s in enumerate(warm):
+        for st in (a, b):
+            st.step(s["q"], s["k"], s["v"], s["beta"], s["ld"])
+        sub = synth.subset(synth.step(w.with_(wid=27), t), np.arange(B * H))
+        orc.eager_step(op, X, sub["q"], sub["k"], sub["v"], sub["beta"], sub["ld"], u_sub)
+    new3 = synth.initial(w.with_(wid=5003))[0][3]
+    for st in (a, b):
+        st.base[3].copy_(dev(new3))
+        st.admit(3)
+    X[0, 6:8] = new3.astype(np.float64)
+    static = [{k_: dev(v_, dt if k_ in ("q", "k", "v") else torch.float32) for k_, v_ in synth.step(w, t).items()}
+              for t in range(M)]
+    outs = [torch.empty(B, H, 128, device="cuda") for _ in range(M)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for t in range(M):
+            s = static[t]
+            b.step(s["q"], s["k"], s["v"], s["beta"], s["ld"], o=outs[t])
+    live = [True] * B
+    rows = lambda s_: slice(s_ * H, (s_ + 1) * H)
+    worst = 0.0
+    for cycle in range(3):
+        if cycle == 1:  # a new request in slot 0, slot 2 finishes
+            new0 = synth.initial(w.with_(wid=5100))[0][0]
+            for st in (a, b):
+                st.base[0].copy_(dev(new0))
+                st.admit(0)
+                st.merge_slot(2)
+                st.release(2)
+            X[0, rows(0)] = new0.astype(np.float64)
+            live[2] = False
+        inputs = [synth.step(w, cycle * M + t) for t in range(M)]
+        for t in range(M):
+            for k_, v_ in inputs[t].items():
+                if v_ is not None:
+                    static[t][k_].copy_(dev(v_, dt if k_ in ("q", "k", "v") else torch.float32))
+        torch.cuda.synchronize()
+        g.replay()
+        ref = [a.step(static[t]["q"], static[t]["k"], static[t]["v"], static[t]["beta"], static[t]["ld"]).clone()
+               for t in range(M)]
+        torch.cuda.synchronize()
+        for t in range(M):
+            for s_ in range(B):
+                if live[s_]:
+                    assert torch.equal(outs[t][s_], ref[t][s_]), (cycle, t, s_)
+            sub = synth.subset(inputs[t], np.arange(B * H))
+            Xkeep = X[0, rows(2)].copy()
+            o_ref = orc.eager_step(op, X, sub["q"], sub["k"], sub["v"], sub["beta"], sub["ld"], u_sub)
+            if not live[2]:
+                X[0, rows(2)] = Xkeep
+            for s_ in range(B):
+                if live[s_]:
+                    worst = max(worst, rel(outs[t][s_].cpu().numpy(), o_ref[0, rows(s_)]))
+        assert torch.equal(a.base, b.base)
+    print(f"[{op} per-slot graph] worst o={worst:.2e}", flush=True)
+    a.close()
+    b.close()
+    assert worst < FP32_TOL
