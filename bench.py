@@ -567,6 +567,8 @@ def main():
     ap.add_argument("--workload", type=int, default=1, choices=[1, 2, 3, 4])
     ap.add_argument("--op", default=None, help="operator of workload 4 (gdn|kda)")
     ap.add_argument("--M", type=int, default=None, help="merge interval (workload 4 sweep)")
+    ap.add_argument("--B", type=int, default=None, help="override the workload's batch (slots)")
+    ap.add_argument("--H", type=int, default=None, help="override the workload's head count")
     ap.add_argument("--rotate", type=int, default=4, help="independent states stepped in turn")
     ap.add_argument("--pool", type=int, default=None, help="distinct input steps staged")
     ap.add_argument("--no-cpu", action="store_true")
@@ -613,15 +615,20 @@ def main():
         w = synth.WORKLOADS[args.workload]
         if args.M:
             w = w.with_(M=args.M)
+    if args.B:
+        w = w.with_(B=args.B)
+    if args.H:
+        w = w.with_(H=args.H)
     K, W, R = args.steps, args.warmup, args.rotate
     pool = args.pool or min(w.steps, 256 if w.B <= 128 else 64)
     res = bench_workload(w, K, W, R, pool, quick=args.quick)
-    traffic = measured_traffic() if (args.workload == 1 and not args.M) else None
+    default_shape = args.workload == 1 and not args.M and not args.B and not args.H
+    traffic = measured_traffic() if default_shape else None
     res["roofline"]["traffic"] = traffic
     log(f"{w.describe()}: {res['wall_ms'] / K * 1e3:.2f} us/step")
 
     others = {}
-    if not args.no_others and args.workload == 1:
+    if not args.no_others and default_shape:
         for wid in (2, 3):
             o = synth.WORKLOADS[wid]
             r = bench_workload(o, K, W, R, min(o.steps, 256), with_staged=False)
