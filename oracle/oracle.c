@@ -50,6 +50,16 @@
  * (merge) and empties it.  GDN's scalar decay is stored here broadcast over
  * the keys, which is the same number in every row.
  *
+ * Full forgetting (a log-decay of -inf, e^ell = 0) is part of the domain of
+ * the eager recurrences.  In the DeltaLog model, a cumulative Lam of -inf
+ * would make a later difference Lam_n - Lam_j undefined (-inf - -inf).  So
+ * the model takes each log-decay at no less than ORC_MIN_LOG_DECAY, where
+ * e^ell is already exactly 0 in fp64: the step still zeroes every older term
+ * exactly, and Lam stays finite (the reading taken for the pages' Lambda
+ * snapshots; the abstract's claim that the model observes the same dense
+ * state as eager decoding fixes the result).  The eager functions use ell
+ * as given.
+ *
  * All arithmetic is IEEE fp64, slot-heads are independent (OpenMP over them).
  * parity pinned: see the CPU test suite (brute-force unrolling, closed forms,
  * special cases, invariants, hand-worked examples).
@@ -64,6 +74,9 @@
 #define ORC_GDN 0
 #define ORC_KDA 1
 #define ORC_RWKV6 2
+
+/* e^x is exactly 0 in fp64 for x below about -745.2 */
+#define ORC_MIN_LOG_DECAY (-800.0)
 
 /* log-decay of key i of slot-head sh */
 static double log_decay(int op, const double *ld, long sh, int dk, int i)
@@ -204,7 +217,8 @@ static void dl_one(int op, int h, long sh, int dk, int dv, int M, int n,
 
     for (int i = 0; i < dk; ++i) {
         double prev = n > 0 ? L[(long)(n - 1) * dk + i] : 0.0;
-        Lnew[i] = prev + log_decay(op, ld, sh, dk, i);
+        double ell = log_decay(op, ld, sh, dk, i);
+        Lnew[i] = prev + (ell < ORC_MIN_LOG_DECAY ? ORC_MIN_LOG_DECAY : ell);
     }
 
     if (op == ORC_RWKV6) {

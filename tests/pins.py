@@ -22,7 +22,9 @@ What pins what:
   DeltaLog model -- M = 1 is eager; after every merge the base equals the
       eager state, for every M; outputs equal eager outputs at every step; a
       forced merge at any log length gives the eager state; the model's
-      logical state equals the eager state between merges.
+      logical state equals the eager state between merges; with full decay
+      (log-decay -inf) and extreme finite decays scattered through the
+      steps it still equals eager decoding, and stays finite.
 """
 from __future__ import annotations
 
@@ -306,8 +308,38 @@ def pin_dl_forced_merge(orc):
             assert np.array_equal(before, m.Xb)
 
 
+def pin_dl_full_decay(orc):
+    """Full forgetting inside a log.  Log-decays of -inf (and of -1e4, where
+    e^ell is 0 as well) at scattered steps, heads and keys: outputs at every
+    step, the base after each merge and the logical state between merges
+    all equal eager decoding, which is pinned on full decay above, and all
+    are finite.  This includes entries appended after a wipe, whose decays
+    are differences of cumulative log-decays."""
+    from oracle import DeltaLogModel
+    rng = np.random.default_rng(27)
+    for op in OPS:
+        T = 14
+        X0, q, k, v, beta, ld, u = _inputs(op, 2, 2, 8, 8, T, 26)
+        ld = ld.copy()
+        pick = rng.uniform(size=ld.shape)
+        ld[pick < 0.15] = -np.inf
+        ld[(pick >= 0.15) & (pick < 0.25)] = -1e4
+        ld[3] = -np.inf  # one step that wipes every slot-head entirely
+        oe, Xe = _eager_all(orc, op, X0, q, k, v, beta, ld, u)
+        assert np.isfinite(oe).all() and np.isfinite(Xe).all()
+        for M in (2, 3, 5, 8):
+            m = DeltaLogModel(orc, op, X0, M)
+            for t in range(T):
+                o = m.step(q[t], k[t], v[t], None if beta is None else beta[t], ld[t], u)
+                assert np.isfinite(o).all(), (op, M, t, "o not finite")
+                assert rel(o, oe[t]) < 1e-11, (op, M, t, "o")
+                X = m.Xb if m.n == 0 else m.logical_state()
+                assert np.isfinite(X).all(), (op, M, t, "state not finite")
+                assert rel(X, Xe[t]) < 1e-11, (op, M, t, "state")
+
+
 ALL_PINS = [
     pin_hand_examples, pin_brute_force, pin_delta_rule, pin_frozen_gemv,
     pin_full_decay, pin_rwkv_prefix_sum, pin_linearity, pin_dl_m1_is_eager,
-    pin_dl_merge_invariant, pin_dl_forced_merge,
+    pin_dl_merge_invariant, pin_dl_forced_merge, pin_dl_full_decay,
 ]

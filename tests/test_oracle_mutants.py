@@ -43,6 +43,8 @@ MUTANTS = [
     ("dl_snapshot_prev", "L[(long)n * dk + i] = Lnew[i];",
      "L[(long)n * dk + i] = Lnew[i] - log_decay(op, ld, sh, dk, i);", 0),
     ("dl_rwkv_read_new_decay", "wq[i] = exp(prev) * q[i];", "wq[i] = exp(Lnew[i]) * q[i];", 0),
+    ("dl_no_log_decay_floor", "Lnew[i] = prev + (ell < ORC_MIN_LOG_DECAY ? ORC_MIN_LOG_DECAY : ell);",
+     "Lnew[i] = prev + ell;", 0),
     ("dl_merge_one_early", "if (n + 1 == M)\n        fold_one(dk, dv, M, M, Xb, a, bl, L);",
      "if (n + 2 == M)\n        fold_one(dk, dv, M, n + 1, Xb, a, bl, L);", 0),
 ]
