@@ -33,7 +33,11 @@
  *   state / base   [B,H,d_k,d_v] fp32, 16-byte aligned
  *   q (r), k       [B,H,d_k]   input dtype          v  [B,H,d_v] input dtype
  *   beta           [B,H] fp32 (GDN, KDA; NULL for RWKV6)
- *   log_decay      GDN [B,H] fp32; KDA, RWKV6 [B,H,d_k] fp32 (natural log, <= 0)
+ *   log_decay      GDN [B,H] fp32; KDA, RWKV6 [B,H,d_k] fp32 (natural log, <= 0).
+ *                  -inf (full forgetting: the step erases the history) is
+ *                  accepted.  Values below -112 act as -112, where e^ell is
+ *                  already exactly 0 in fp32; this keeps the log's cumulative
+ *                  decays finite.
  *   u              RWKV6 bonus [H,d_k] fp32 (NULL for GDN, KDA)
  *   o              [B,H,d_v] fp32, 16-byte aligned
  *   workspace      dl_workspace_bytes() bytes, 256-byte aligned; holds the log,

@@ -85,6 +85,15 @@ template <int FROM> __device__ __forceinline__ float wave_sum_from(float x)
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Full forgetting.  A log-decay of -inf (e^ell = 0: the step erases the
+// history) would make the cumulative Lam infinite, and a later difference
+// Lam' - Lam_j would be -inf - (-inf), which is undefined.  Every log-decay is
+// therefore taken at no less than kMinLogDecay.  At that value e^ell is
+// already exactly 0 in fp32, so such a step still erases every older term
+// exactly, while Lam stays finite.  A NaN passes through unchanged.
+constexpr float kMinLogDecay = -112.f;
+__device__ __forceinline__ float floor_log_decay(float x) { return x < kMinLogDecay ? kMinLogDecay : x; }
+
 // Raw buffer resources: a base, a size in bytes, and loads at a 32-bit byte
 // offset (per lane) plus a wave-uniform offset.  An access at or past the size
 // reads zero and touches no memory; stores there are dropped.
@@ -294,7 +303,7 @@ __global__ __launch_bounds__(256) void replay_prep_kernel(StepArgs a)
         // Lam_{n-1} is entry n-1 of the log (0 when the log is empty)
         lp[c] = OP == GDN ? (n > 0 ? buf_ldf(lr, (unsigned)(n - 1) * 4u) : 0.f)
                           : buf_ld_in<float>(lr, (n > 0 && i < DK) ? (unsigned)((n - 1) * DK + i) : kSkipElem);
-        lw[c] = lp[c] + (OP == GDN ? a.ld[sh] : (i < DK ? a.ld[(long)sh * DK + i] : 0.f));
+        lw[c] = lp[c] + floor_log_decay(OP == GDN ? a.ld[sh] : (i < DK ? a.ld[(long)sh * DK + i] : 0.f));
     }
 
     float *coef = a.coef + (long)sh * a.cstride;
@@ -495,7 +504,8 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
     float gprev = 0.f, gnew = 0.f;
     if (OP == GDN) {
         gprev = (MODE != EAGER && n > 0) ? L[n - 1] : 0.f;
-        gnew = MODE == EAGER ? a.ld[sh] : STAGED ? L[n] : FOLDS ? gprev : gprev + a.ld[sh];
+        gnew = MODE == EAGER ? floor_log_decay(a.ld[sh])
+             : STAGED ? L[n] : FOLDS ? gprev : gprev + floor_log_decay(a.ld[sh]);
     }
     // This tile's shard of the n logged value-side factors.
     const rsrc_t b_r = make_rsrc(static_cast<const char *>(a.blog) + (long)sh * M * DV * BS,
@@ -566,7 +576,7 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
         mk[j] = cvt1<TIn>(rk_[j], tid + j * NT);
         mprev[j] = n > 0 ? __uint_as_float(rprev[j]) : 0.f; // Lam_{-1} = 0
         mcur[j] = __uint_as_float(rcur[j]);
-        mell[j] = __uint_as_float(rell[j]);
+        mell[j] = floor_log_decay(__uint_as_float(rell[j]));
         mu[j] = __uint_as_float(ru[j]);
     }
     float lnew_[RW]; // Lam' per row, kept for the key-side append at the end

@@ -23,7 +23,16 @@ FP32_TOL = 2e-4
 
 
 def rel(x, ref) -> float:
-    x, ref = np.asarray(x, np.float64), np.asarray(ref, np.float64)
+    """Max-abs relative error; inf where x holds a NaN or inf that the
+    reference does not (so running maxima, which skip NaN, cannot hide one)."""
+    x, ref = np.broadcast_arrays(np.asarray(x, np.float64), np.asarray(ref, np.float64))
+    fin = np.isfinite(ref)
+    if (np.isfinite(x) != fin).any():
+        return float("inf")
+    if not fin.all():
+        x, ref = x[fin], ref[fin]
+    if ref.size == 0:
+        return 0.0
     den = np.max(np.abs(ref))
     return float(np.max(np.abs(x - ref)) / den) if den > 0 else float(np.max(np.abs(x - ref)))
 

@@ -745,3 +745,65 @@ def test_graph_capture_per_slot(orc, op):
     a.close()
     b.close()
     assert worst < FP32_TOL
+
+
+def _with_full_decay(s: dict, t: int, rng) -> dict:
+    """Step inputs with full forgetting mixed in: log-decay -inf on ~15% of
+    the (slot-head[, key]) entries and -1e4 (e^ell = 0 as well) on ~10%; at
+    step 3 every entry is -inf, which wipes every state."""
+    s = dict(s)
+    ld = s["ld"].copy()
+    pick = rng.uniform(size=ld.shape)
+    ld[pick < 0.15] = -np.inf
+    ld[(pick >= 0.15) & (pick < 0.25)] = -1e4
+    if t == 3:
+        ld[...] = -np.inf
+    s["ld"] = ld
+    return s
+
+
+@needs_gpu
+@pytest.mark.parametrize("op", ["gdn", "kda", "rwkv6"])
+@pytest.mark.parametrize("path", ["fused", "staged", "eager", "per-slot"])
+def test_full_decay(orc, op, path):
+    """Full forgetting (log-decay -inf) and extreme finite decays inside the
+    log: the steps after a wipe replay entries whose decays are differences
+    of cumulative log-decays.  M=4, 14 steps, then a forced merge; every
+    output and every merged base against the eager oracle, all finite."""
+    w = synth.Workload(22, op, 2, 3, 64, 64, 4, 14, "bf16")
+    rng = np.random.default_rng(22)
+    if path != "per-slot":
+        run = ParityRun(w, eager=path == "eager", orc=orc)
+        for t in range(w.steps):
+            run.step(_with_full_decay(synth.step(w, t), t, rng), staged=path == "staged")
+        if path != "eager":
+            run.merge()
+        _report(run, f"full decay {op} {path}")
+        run.close()
+        return
+    import recurrent_state_update_amd as rsu
+    X0, u = synth.initial(w)
+    BH = w.B * w.H
+    st = rsu.DeltaLogState(op, w.B, w.H, 64, 64, w.M, dtype=torch.bfloat16, base=dev(X0), u=dev(u))
+    st.enable_slots()
+    X = X0.reshape(BH, 64, 64).astype(np.float64)[None].copy()
+    u_sub = None if u is None else u[np.arange(BH) % w.H].astype(np.float64)
+    worst = 0.0
+    for t in range(w.steps):
+        if t == 2:  # slot 1 restarts from a fresh seeded state: the slots' logs fall out of step
+            new = synth.initial(w.with_(wid=2200))[0][1]
+            st.base[1].copy_(dev(new))
+            st.admit(1)
+            X[0, w.H:2 * w.H] = new.astype(np.float64)
+        s = _with_full_decay(synth.step(w, t), t, rng)
+        d_ = {k_: dev(v_, torch.bfloat16 if k_ in ("q", "k", "v") else torch.float32)
+              for k_, v_ in s.items()}
+        o = st.step(d_["q"], d_["k"], d_["v"], d_["beta"], d_["ld"])
+        sub = synth.subset(s, np.arange(BH))
+        o_ref = orc.eager_step(op, X, sub["q"], sub["k"], sub["v"], sub["beta"], sub["ld"], u_sub)
+        worst = max(worst, rel(o.reshape(BH, 64).cpu().numpy(), o_ref[0]))
+    st.merge()
+    worst_S = rel(st.base.reshape(BH, 64, 64).cpu().numpy(), X[0])
+    st.close()
+    print(f"[full decay {op} per-slot] worst o={worst:.2e} S={worst_S:.2e}", flush=True)
+    assert worst < FP32_TOL and worst_S < FP32_TOL
