@@ -492,10 +492,11 @@ def bench_workload(w, K, W, R, pool, with_eager=True, with_staged=True, quick=Fa
         _, launches, _ = run_deltalog(w, inp, sts, K, W, instrument=True, path="fused")
     res["direct_launch"] = dict(value=round(w.BH * K / (wall * 1e-3), 1), ms_per_step=round(wall / K, 5),
                                 achieved_GBs=round(direct_bytes / (wall / K * 1e-3) / 1e9, 1))
-    app = [x[0] for x in launches if not x[2]]
-    mer = [x[0] for x in launches if x[2]]
-    res["roofline"]["event_bracketed_us"] = dict(append=round(1e3 * sum(app) / max(len(app), 1), 2),
-                                                 merge=round(1e3 * sum(mer) / max(len(mer), 1), 2))
+    if launches:  # not taken in quick runs
+        app = [x[0] for x in launches if not x[2]]
+        mer = [x[0] for x in launches if x[2]]
+        res["roofline"]["event_bracketed_us"] = dict(append=round(1e3 * sum(app) / max(len(app), 1), 2),
+                                                     merge=round(1e3 * sum(mer) / max(len(mer), 1), 2))
     if R > 1 and not quick:
         one, _, _ = run_deltalog(w, inp, sts[:1], K, W, instrument=False)
         res["single_state_value"] = round(w.BH * K / (one * 1e-3), 1)
