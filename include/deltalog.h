@@ -50,7 +50,10 @@
  * Errors and ownership.  Every call returns a dl_status and never aborts or
  * throws.  Arguments are validated on the host before any HIP call (so bad
  * arguments are reported the same way with or without a GPU).  Kernel launch
- * failures return DL_E_HIP.  All calls are asynchronous on `stream` (a
+ * failures return DL_E_HIP.  A buffer that a call writes (o; base and
+ * workspace, through the handle; S of the eager step) must not overlap any
+ * other buffer of the call, or the call returns DL_E_INVALID; the read-only
+ * inputs may alias each other.  All calls are asynchronous on `stream` (a
  * hipStream_t; NULL = the default stream): a DL_OK return says the work was
  * queued, not that it finished.  The library never allocates or frees device
  * memory; the handle is host memory owned by the library (create/destroy).

@@ -111,6 +111,58 @@ dl_status check_step_ptrs(int op, int dtype, const void *q, const void *k, const
     return DL_OK;
 }
 
+// Byte ranges of a call's buffers.  A buffer the call writes (o, the base,
+// the workspace) must not overlap any other buffer of the call: kernels
+// would read it while other workgroups write it.  Inputs may alias each
+// other (all are read-only).
+struct Span {
+    const void *p;
+    size_t bytes;
+};
+
+bool overlap(Span a, Span b)
+{
+    if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0)
+        return false;
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a.p), y = reinterpret_cast<uintptr_t>(b.p);
+    return x < y + b.bytes && y < x + a.bytes;
+}
+
+dl_status check_overlaps(const Span *writes, int nw, const Span *reads, int nr)
+{
+    for (int i = 0; i < nw; ++i) {
+        for (int j = i + 1; j < nw; ++j)
+            if (overlap(writes[i], writes[j]))
+                return DL_E_INVALID;
+        for (int j = 0; j < nr; ++j)
+            if (overlap(writes[i], reads[j]))
+                return DL_E_INVALID;
+    }
+    return DL_OK;
+}
+
+// The buffers of one step on a B x H x d_k x d_v shape.
+struct StepSpans {
+    Span q, k, v, beta, ld, u, o, base;
+};
+
+StepSpans step_spans(int op, int dtype, long B, long H, int dk, int dv, const void *q, const void *k,
+                     const void *v, const float *beta, const float *ld, const float *u, const float *o,
+                     const float *base)
+{
+    const size_t es = dtype == DL_BF16 ? 2 : 4, BH = (size_t)(B * H);
+    StepSpans sp;
+    sp.q = {q, BH * dk * es};
+    sp.k = {k, BH * dk * es};
+    sp.v = {v, BH * dv * es};
+    sp.beta = {beta, BH * 4};
+    sp.ld = {ld, (op == DL_OP_GDN ? BH : BH * dk) * 4};
+    sp.u = {u, (size_t)H * dk * 4};
+    sp.o = {o, BH * dv * 4};
+    sp.base = {base, BH * dk * dv * 4};
+    return sp;
+}
+
 dl::StepArgs make_args(const dl_state *s)
 {
     dl::StepArgs a{};
@@ -152,6 +204,18 @@ hipError_t launch_step(int op, int dtype, int dk, int dv, int mode, const dl::St
     }
 }
 
+// o, the base and the workspace against each other and against the step's
+// inputs (ld may be NULL: the two-stage AppendDecode does not read it)
+dl_status check_handle_step_overlaps(const dl_state *s, const void *q, const void *k, const void *v,
+                                     const float *beta, const float *ld, const float *o)
+{
+    const StepSpans sp = step_spans(s->op, s->dtype, s->B, s->H, s->dk, s->dv, q, k, v, beta, ld, s->u, o,
+                                    s->base);
+    const Span w[3] = {sp.o, sp.base, {s->ws, s->lay.total}};
+    const Span r[6] = {sp.q, sp.k, sp.v, sp.beta, sp.ld, sp.u};
+    return check_overlaps(w, 3, r, 6);
+}
+
 } // namespace
 
 extern "C" {
@@ -176,6 +240,13 @@ dl_status dl_state_create(int B, int H, int d_k, int d_v, int M, dl_op op, dl_dt
         return DL_E_INVALID;
     if (!aligned(base, 16) || !aligned(workspace, 256) || (u && !aligned(u, 4)))
         return DL_E_ALIGN;
+    {
+        const StepSpans sp = step_spans(op, in_dtype, B, H, d_k, d_v, nullptr, nullptr, nullptr, nullptr,
+                                        nullptr, op == DL_OP_RWKV6 ? u : nullptr, nullptr, base);
+        const Span w[2] = {sp.base, {workspace, dl::workspace_layout(B, H, d_k, d_v, M, op, in_dtype).total}};
+        if (check_overlaps(w, 2, &sp.u, 1) != DL_OK)
+            return DL_E_INVALID;
+    }
     dl_state *s = new (std::nothrow) dl_state;
     int *t0 = new (std::nothrow) int[B];
     if (!s || !t0) {
@@ -215,6 +286,14 @@ dl_status dl_replay_prep(dl_state *s, const void *q, const void *k, const float 
     const size_t es = s->dtype == DL_BF16 ? 2 : 4;
     if (!aligned(q, es) || !aligned(k, es) || !aligned(log_decay, 4))
         return DL_E_ALIGN;
+    {
+        const StepSpans sp = step_spans(s->op, s->dtype, s->B, s->H, s->dk, s->dv, q, k, nullptr, nullptr,
+                                        log_decay, nullptr, nullptr, nullptr);
+        const Span w = {s->ws, s->lay.total};
+        const Span r[3] = {sp.q, sp.k, sp.ld};
+        if (check_overlaps(&w, 1, r, 3) != DL_OK)
+            return DL_E_INVALID;
+    }
     dl::StepArgs a = make_args(s);
     a.q = q;
     a.k = k;
@@ -233,7 +312,9 @@ dl_status dl_append_decode(dl_state *s, const void *q, const void *k, const void
     if (!s->prepped || s->per_slot)
         return DL_E_STATE;
     // this stage does not read the log-decay: ReplayPrep stored Lam'
-    const dl_status st = check_step_ptrs(s->op, s->dtype, q, k, v, beta, nullptr, o, false);
+    dl_status st = check_step_ptrs(s->op, s->dtype, q, k, v, beta, nullptr, o, false);
+    if (st == DL_OK)
+        st = check_handle_step_overlaps(s, q, k, v, beta, nullptr, o);
     if (st != DL_OK)
         return st;
     dl::StepArgs a = make_args(s);
@@ -258,7 +339,9 @@ dl_status dl_decode_step(dl_state *s, const void *q, const void *k, const void *
         return DL_E_INVALID;
     if (s->prepped)
         return DL_E_STATE;
-    const dl_status st = check_step_ptrs(s->op, s->dtype, q, k, v, beta, log_decay, o, true);
+    dl_status st = check_step_ptrs(s->op, s->dtype, q, k, v, beta, log_decay, o, true);
+    if (st == DL_OK)
+        st = check_handle_step_overlaps(s, q, k, v, beta, log_decay, o);
     if (st != DL_OK)
         return st;
     dl::StepArgs a = make_args(s);
@@ -429,6 +512,14 @@ dl_status dl_eager_step(dl_op op, int B, int H, int d_k, int d_v, dl_dtype in_dt
         return st;
     if (!aligned(S, 16) || (u && !aligned(u, 4)))
         return DL_E_ALIGN;
+    {
+        const StepSpans sp = step_spans(op, in_dtype, B, H, d_k, d_v, q, k, v, beta, log_decay,
+                                        op == DL_OP_RWKV6 ? u : nullptr, o, S);
+        const Span w[2] = {sp.o, sp.base};
+        const Span r[6] = {sp.q, sp.k, sp.v, sp.beta, sp.ld, sp.u};
+        if (check_overlaps(w, 2, r, 6) != DL_OK)
+            return DL_E_INVALID;
+    }
     dl::StepArgs a{};
     a.BH = B * H;
     a.H = H;

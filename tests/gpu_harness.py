@@ -84,10 +84,16 @@ class ParityRun:
         self.worst_S = 0.0
         self.checked_S = 0
 
-    def step(self, s: dict | None = None, staged: bool = False):
+    def step(self, s: dict | None = None, staged: bool = False, alias_qk: bool = False):
+        """One step; with alias_qk, q is passed as k's device buffer (the
+        oracle is fed s["k"] for both)."""
         w = self.w
         s = s if s is not None else synth.step(w, self.t)
+        if alias_qk:
+            s = dict(s, q=s["k"])
         q, k, v = dev(s["q"], self.dt), dev(s["k"], self.dt), dev(s["v"], self.dt)
+        if alias_qk:
+            q = k
         beta, ld = dev(s["beta"]), dev(s["ld"])
         if self.eager:
             o = self.rsu.eager_step(w.op, self.base, q, k, v, beta, ld, self.u_dev)

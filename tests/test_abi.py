@@ -187,3 +187,39 @@ def test_binding_validates_eager_inputs():
     q = torch.zeros(1, 2, 16)
     with pytest.raises(ValueError):
         rsu.eager_step("gdn", S, q, q, q, None, None)
+
+
+def test_overlapping_buffers_are_rejected():
+    """A buffer a call writes (o, base, workspace; S of the eager step) may not
+    overlap another buffer of the call: the call returns DL_E_INVALID before
+    any launch.  B=2 H=3 d=16 fp32: the base is 6 KiB, o 384 B."""
+    s = 0
+    # at creation: the base against the workspace, u against both
+    assert _create(ws=BASE + 4096)[0] == INVALID
+    assert _create(base=WS + 256)[0] == INVALID
+    assert _create(op=RWKV6, u=BASE + 64)[0] == INVALID
+    assert _create(op=RWKV6, u=WS + 1024)[0] == INVALID
+    st, h = _create(ws=BASE + 6 * 16 * 16 * 4)  # adjacent ranges are fine
+    assert st == OK
+    rsu.dl_state_destroy(h)
+    st, h = _create(op=KDA)
+    assert st == OK
+    try:
+        d = rsu.dl_decode_step
+        assert d(h, Q, K, V, BETA, LD, BASE + 1024, s) == INVALID     # o inside the base
+        assert d(h, Q, K, V, BETA, LD, WS + 4096, s) == INVALID       # o inside the workspace
+        assert d(h, Q, K, V, BETA, LD, Q + 16, s) == INVALID          # o over q
+        assert d(h, Q, K, V, BETA, LD, LD + 32, s) == INVALID         # o over the log-decay
+        assert d(h, Q, K, V, BETA, LD, V - 16, s) == INVALID          # o ends inside v
+        assert d(h, BASE + 64, K, V, BETA, LD, O, s) == INVALID       # q inside the base
+        assert d(h, Q, WS, V, BETA, LD, O, s) == INVALID              # k inside the workspace
+        assert d(h, Q, K, V, BETA, WS + 512, O, s) == INVALID         # log-decay inside the workspace
+        assert rsu.dl_replay_prep(h, Q, WS + 256, LD, s) == INVALID   # ReplayPrep writes the workspace
+        assert rsu.dl_replay_prep(h, Q, K, WS, s) == INVALID
+    finally:
+        rsu.dl_state_destroy(h)
+    e = rsu.dl_eager_step
+    assert e(GDN, 2, 3, 16, 16, F32, BASE, Q, K, V, BETA, LD, None, BASE + 512, s) == INVALID  # o in S
+    assert e(GDN, 2, 3, 16, 16, F32, BASE, BASE, K, V, BETA, LD, None, O, s) == INVALID       # q in S
+    assert e(RWKV6, 2, 3, 16, 16, F32, BASE, Q, K, V, None, LD, BASE + 16, O, s) == INVALID   # u in S
+    assert e(GDN, 2, 3, 16, 16, F32, BASE, Q, K, V, BETA, LD, None, K + 256, s) == INVALID   # o over k

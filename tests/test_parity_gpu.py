@@ -807,3 +807,18 @@ def test_full_decay(orc, op, path):
     st.close()
     print(f"[full decay {op} per-slot] worst o={worst:.2e} S={worst_S:.2e}", flush=True)
     assert worst < FP32_TOL and worst_S < FP32_TOL
+
+
+@needs_gpu
+@pytest.mark.parametrize("op", ["gdn", "rwkv6"])
+def test_inputs_may_alias(orc, op):
+    """Read-only inputs may share memory: q and k passed as the same buffer
+    (o_t then reads the state with the key it was just written with). M=4,
+    9 steps, the eager oracle fed the same aliased inputs."""
+    w = synth.Workload(23, op, 2, 3, 64, 64, 4, 9, "bf16")
+    run = ParityRun(w, orc=orc)
+    for t in range(w.steps):
+        run.step(alias_qk=True)
+    run.merge()
+    _report(run, f"q aliases k, {op}")
+    run.close()
