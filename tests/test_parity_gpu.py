@@ -822,3 +822,57 @@ def test_inputs_may_alias(orc, op):
     run.merge()
     _report(run, f"q aliases k, {op}")
     run.close()
+
+
+@needs_gpu
+def test_concurrent_handles_on_separate_streams(orc):
+    """Two handles (GDN and KDA) stepped at the same time from two host
+    threads, each on its own stream (default priority): the library keeps no
+    state outside its handles, so both runs match the oracle.  M=4, 10 steps
+    each, then a merge; every output and both merged bases."""
+    import threading
+    import recurrent_state_update_amd as rsu
+    jobs = [("gdn", 24), ("kda", 25)]
+    results, errors = {}, []
+
+    def worker(i, op, wid):
+        try:
+            w = synth.Workload(wid, op, 2, 3, 64, 64, 4, 10, "bf16")
+            stream = torch.cuda.Stream()
+            with torch.cuda.stream(stream):
+                X0, u = synth.initial(w)
+                base = dev(X0)
+                st = rsu.DeltaLogState(op, w.B, w.H, 64, 64, w.M, dtype=torch.bfloat16, base=base,
+                                       u=dev(u))
+                outs = []
+                for t in range(w.steps):
+                    s = synth.step(w, t)
+                    d_ = {k_: dev(v_, torch.bfloat16 if k_ in ("q", "k", "v") else torch.float32)
+                          for k_, v_ in s.items()}
+                    outs.append(st.step(d_["q"], d_["k"], d_["v"], d_["beta"], d_["ld"]).clone())
+                st.merge()
+            stream.synchronize()
+            results[i] = (w, X0, [o.cpu().numpy() for o in outs], base.cpu().numpy())
+            st.close()
+        except Exception as exc:  # re-raised in the main thread
+            errors.append(exc)
+
+    threads = [threading.Thread(target=worker, args=(i, op, wid)) for i, (op, wid) in enumerate(jobs)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    if errors:
+        raise errors[0]
+    for i, (op, _) in enumerate(jobs):
+        w, X0, outs, base = results[i]
+        BH = w.B * w.H
+        X = X0.reshape(BH, 64, 64).astype(np.float64)[None].copy()
+        worst = 0.0
+        for t in range(w.steps):
+            sub = synth.subset(synth.step(w, t), np.arange(BH))
+            o_ref = orc.eager_step(op, X, sub["q"], sub["k"], sub["v"], sub["beta"], sub["ld"], None)
+            worst = max(worst, rel(outs[t].reshape(BH, 64), o_ref[0]))
+        worst_S = rel(base.reshape(BH, 64, 64), X[0])
+        print(f"[concurrent {op}] worst o={worst:.2e} S={worst_S:.2e}", flush=True)
+        assert worst < FP32_TOL and worst_S < FP32_TOL
