@@ -876,3 +876,21 @@ def test_concurrent_handles_on_separate_streams(orc):
         worst_S = rel(base.reshape(BH, 64, 64), X[0])
         print(f"[concurrent {op}] worst o={worst:.2e} S={worst_S:.2e}", flush=True)
         assert worst < FP32_TOL and worst_S < FP32_TOL
+
+
+@needs_gpu
+@pytest.mark.parametrize("op", ["gdn", "kda", "rwkv6"])
+@pytest.mark.parametrize("path", ["fused", "staged"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_longest_log_at_d128(orc, op, path, dtype):
+    """The largest LDS footprint a lockstep launch has: M=32 at d_k=d_v=128
+    (a 32-entry fold table and value shard per tile; the log shard takes a
+    second staging pass and the coefficients a per-wave loop past the first
+    8 entries).  Two merge cycles plus 5 steps, then a forced merge."""
+    w = synth.Workload(26, op, 2, 3, 128, 128, 32, 69, dtype)
+    run = ParityRun(w, orc=orc)
+    for _ in range(w.steps):
+        run.step(staged=path == "staged")
+    run.merge()
+    _report(run, f"{op} M=32 d=128 {path} {dtype}")
+    run.close()
