@@ -169,7 +169,10 @@ int dl_suggest_merge_interval(int B, int H, int d_k, int d_v, dl_op op, dl_dtype
 /* Switch a handle to per-slot logs.  Needs an empty log (a fresh handle, or
  * after dl_merge); every slot starts empty.  Afterwards dl_decode_step and
  * dl_merge act per slot; dl_replay_prep, dl_append_decode, dl_set_log_len and
- * dl_state_reset return DL_E_STATE. */
+ * dl_state_reset return DL_E_STATE.  Checkpoint of such a handle: dl_merge
+ * (every active slot's log is then empty), save `base`; to restore, create a
+ * handle over the saved base, enable per-slot logs and release the slots
+ * that were released.  It continues exactly as the original would. */
 dl_status dl_state_enable_slots(dl_state *s, void *stream);
 
 /* Admit a new request into `slot` (also one released before): drop the

@@ -894,3 +894,76 @@ def test_longest_log_at_d128(orc, op, path, dtype):
     run.merge()
     _report(run, f"{op} M=32 d=128 {path} {dtype}")
     run.close()
+
+
+@needs_gpu
+@pytest.mark.parametrize("op", ["gdn", "kda", "rwkv6"])
+def test_checkpoint_restore_per_slot(orc, op):
+    """Checkpoint of a handle with per-slot logs: dl_merge folds every active
+    slot's log (all logs empty, released slots untouched); a new handle over
+    a copy of the base, with per-slot logs enabled and the same slots
+    released, then continues bit-identically to the original, through
+    admissions and each slot's own merges.  Both match the oracle."""
+    import recurrent_state_update_amd as rsu
+    B, H, M = 4, 2, 4
+    w = synth.Workload(27, op, B, H, 64, 64, M, 15, "bf16")
+    X0, u = synth.initial(w)
+    dt = in_dtype(w)
+    a = rsu.DeltaLogState(op, B, H, 64, 64, M, dtype=dt, base=dev(X0), u=dev(u))
+    a.enable_slots()
+    X = X0.reshape(B * H, 64, 64).astype(np.float64)[None].copy()
+    u_sub = None if u is None else u[np.arange(B * H) % H].astype(np.float64)
+
+    def inputs(t):
+        s = synth.step(w, t)
+        return s, (dev(s["q"], dt), dev(s["k"], dt), dev(s["v"], dt), dev(s["beta"]), dev(s["ld"]))
+
+    def fresh(b, t):  # a new request's seeded initial state for slot b
+        return synth.initial(w.with_(wid=2700 + 10 * t + b))[0][b]
+
+    def oracle_step(s):
+        sub = synth.subset(s, np.arange(B * H))
+        return orc.eager_step(op, X, sub["q"], sub["k"], sub["v"], sub["beta"], sub["ld"], u_sub)[0]
+
+    worst = 0.0
+    for t in range(6):           # slot 1 admitted late, slot 3 released: logs out of step
+        if t == 2:
+            new = fresh(1, t)
+            a.base[1].copy_(dev(new))
+            a.admit(1)
+            X[0, H:2 * H] = new.astype(np.float64)
+        if t == 3:
+            a.release(3)
+        s, d_ = inputs(t)
+        o = a.step(*d_).reshape(B * H, 64).cpu().numpy()
+        o_ref = oracle_step(s)
+        live = np.arange(B * H) < 3 * H if t >= 3 else np.ones(B * H, bool)
+        worst = max(worst, rel(o[live], o_ref[live]))
+    a.merge()                    # the checkpoint: every active slot's log is empty
+    b = rsu.DeltaLogState(op, B, H, 64, 64, M, dtype=dt, base=a.base.clone(), u=dev(u))
+    b.enable_slots()
+    b.release(3)
+    for t in range(6, w.steps):
+        if t == 9:               # a new request in the released slot, on both handles
+            new = fresh(3, t)
+            a.base[3].copy_(dev(new))
+            b.base[3].copy_(dev(new))
+            a.admit(3)
+            b.admit(3)
+            X[0, 3 * H:] = new.astype(np.float64)
+        s, d_ = inputs(t)
+        # zeroed outputs: a released slot's rows are left as they are
+        oa = a.step(*d_, o=torch.zeros(B, H, 64, device="cuda"))
+        ob = b.step(*d_, o=torch.zeros(B, H, 64, device="cuda"))
+        assert torch.equal(oa, ob), (op, t)
+        o_ref = oracle_step(s)
+        live = np.arange(B * H) < 3 * H if t < 9 else np.ones(B * H, bool)
+        worst = max(worst, rel(ob.reshape(B * H, 64).cpu().numpy()[live], o_ref[live]))
+    a.merge()
+    b.merge()
+    assert torch.equal(a.base, b.base)
+    worst_S = rel(b.base.reshape(B * H, 64, 64).cpu().numpy(), X[0])
+    a.close()
+    b.close()
+    print(f"[checkpoint per-slot {op}] worst o={worst:.2e} S={worst_S:.2e}", flush=True)
+    assert worst < FP32_TOL and worst_S < FP32_TOL
