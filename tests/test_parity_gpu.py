@@ -155,7 +155,7 @@ def test_staged_and_fused_paths(orc, op):
 
 @needs_gpu
 @pytest.mark.parametrize("op", ["gdn", "kda", "rwkv6"])
-@pytest.mark.parametrize("M", [3, 8, 32])
+@pytest.mark.parametrize("M", [1, 3, 8, 32])
 def test_staged_path_merge_intervals(orc, op, M):
     """The two-stage ReplayPrep/AppendDecode path over whole merge cycles."""
     w = synth.Workload(16, op, 3, 5, 64, 128, M, 2 * M + 1, "bf16")
