@@ -9,6 +9,8 @@ sequence of schedule events:
 Every output of a live slot is checked against the fp64 eager oracle on the
 same inputs; so is every base that a merge makes observable (forced merges,
 slot merges, the final merge).  Bar: the fp32 bound FP32_TOL."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -19,7 +21,9 @@ from gpu_harness import FP32_TOL, ParityRun, dev, in_dtype, rel
 pytestmark = pytest.mark.gpu
 needs_gpu = pytest.mark.skipif(not torch.cuda.is_available(), reason="no GPU")
 
-N_CASES = 48
+# cases [FIRST, FIRST + N_CASES); a wider sweep: DL_FUZZ_FIRST=1000 DL_FUZZ_CASES=1000
+FIRST = int(os.environ.get("DL_FUZZ_FIRST", "0"))
+N_CASES = int(os.environ.get("DL_FUZZ_CASES", "48"))
 PATHS = ("fused", "staged", "eager", "per-slot")
 
 
@@ -96,7 +100,7 @@ def _per_slot(w, rng, orc):
 
 
 @needs_gpu
-@pytest.mark.parametrize("i", range(N_CASES))
+@pytest.mark.parametrize("i", range(FIRST, FIRST + N_CASES))
 def test_random_case(orc, i):
     w, path, rng = draw(i)
     print(f"[fuzz {i}] {w.describe()} {path}", flush=True)
