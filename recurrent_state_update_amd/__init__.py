@@ -179,6 +179,18 @@ def dl_status_string(st) -> str:
 
 # ------------------------------------------------------------ torch helpers --
 
+def _op_id(op) -> int:
+    if op not in OPS:
+        raise ValueError(f"unknown operator {op!r}: want one of {sorted(OPS)}")
+    return OPS[op]
+
+
+def _dtype_id(dtype) -> int:
+    if dtype not in DTYPES:
+        raise ValueError(f"unsupported input dtype {dtype}: want torch.bfloat16 or torch.float32")
+    return DTYPES[dtype]
+
+
 def _want(t, name, dtype, shape, device=None):
     if t is None:
         raise ValueError(f"{name} is required")
@@ -199,7 +211,7 @@ class DeltaLogState:
                  u: torch.Tensor | None = None, device="cuda"):
         self.op, self.B, self.H, self.d_k, self.d_v, self.M = op, B, H, d_k, d_v, M
         self.dtype = dtype
-        opi, dti = OPS[op], DTYPES[dtype]
+        opi, dti = _op_id(op), _dtype_id(dtype)
         nbytes = dl_workspace_bytes(B, H, d_k, d_v, M, opi, dti)
         if nbytes == 0:
             raise ValueError(f"unsupported DeltaLog shape {op} B={B} H={H} d_k={d_k} d_v={d_v} M={M}")
@@ -299,6 +311,7 @@ def eager_step(op: str, S, q, k, v, beta, log_decay, u=None, o=None, stream=None
     """The eager baseline: one step that reads and rewrites S [B,H,d_k,d_v]."""
     B, H, dk, dv = S.shape
     dtype = q.dtype
+    opi, dti = _op_id(op), _dtype_id(dtype)
     dev = S.device
     _want(S, "S", torch.float32, (B, H, dk, dv))
     _want(q, "q", dtype, (B, H, dk), dev)
@@ -312,6 +325,6 @@ def eager_step(op: str, S, q, k, v, beta, log_decay, u=None, o=None, stream=None
     if o is None:
         o = torch.empty(B, H, dv, dtype=torch.float32, device=dev)
     _want(o, "o", torch.float32, (B, H, dv), dev)
-    _check(dl_eager_step(OPS[op], B, H, dk, dv, DTYPES[dtype], S, q, k, v, beta, log_decay, u, o,
+    _check(dl_eager_step(opi, B, H, dk, dv, dti, S, q, k, v, beta, log_decay, u, o,
                          stream), "dl_eager_step")
     return o

@@ -135,6 +135,17 @@ def test_binding_refuses_host_tensors():
                           base=torch.zeros(1, 2, 16, 16))
 
 
+def test_binding_names_bad_operator_and_dtype():
+    import torch
+    with pytest.raises(ValueError, match="unknown operator"):
+        rsu.DeltaLogState("mamba", 1, 2, 16, 16, 4)
+    with pytest.raises(ValueError, match="unsupported input dtype"):
+        rsu.DeltaLogState("gdn", 1, 2, 16, 16, 4, dtype=torch.float16)
+    S = torch.zeros(1, 2, 16, 16)
+    with pytest.raises(ValueError, match="unsupported input dtype"):
+        rsu.eager_step("gdn", S, torch.zeros(1, 2, 16, dtype=torch.float16), None, None, None, None)
+
+
 def test_suggest_merge_interval():
     """The suggested M minimises the documented per-step byte model: check it
     against the model's stationary point sqrt(2 (P - E_app) / (E_key*tiles +
