@@ -967,3 +967,26 @@ def test_checkpoint_restore_per_slot(orc, op):
     b.close()
     print(f"[checkpoint per-slot {op}] worst o={worst:.2e} S={worst_S:.2e}", flush=True)
     assert worst < FP32_TOL and worst_S < FP32_TOL
+
+
+@needs_gpu
+@pytest.mark.parametrize("op", ["gdn", "kda", "rwkv6"])
+@pytest.mark.parametrize("path", ["fused", "staged"])
+def test_full_decay_long_log(orc, op, path):
+    """Repeated full forgetting within one long log (M=32): 30% of the
+    (slot-head[, key]) entries take log-decay -inf at every step, so the
+    cumulative decays reach many times the floor before a merge and the
+    entries appended after a wipe take their decays as differences of large
+    numbers.  70 steps (two merges), then a forced merge."""
+    w = synth.Workload(28, op, 2, 3, 64, 64, 32, 70, "bf16")
+    rng = np.random.default_rng(28)
+    run = ParityRun(w, orc=orc)
+    for t in range(w.steps):
+        s = dict(synth.step(w, t))
+        ld = s["ld"].copy()
+        ld[rng.uniform(size=ld.shape) < 0.3] = -np.inf
+        s["ld"] = ld
+        run.step(s, staged=path == "staged")
+    run.merge()
+    _report(run, f"full decay, long log, {op} {path}")
+    run.close()
