@@ -533,6 +533,32 @@ def bench_workload(w, K, W, R, pool, with_eager=True, with_staged=True, quick=Fa
     return res
 
 
+def deep_rotation(w, K: int, W: int, R: int, pool: int) -> dict:
+    """The headline steps over R states instead of the default 4, as a deep
+    model's many layers would step them: R x (state + log) far exceeds the
+    Infinity Cache, so the log entries, like the state, come from HBM.
+    DeltaLog and eager, both graph-replayed, over a whole number of merge
+    cycles of every state (K rounded up to a multiple of R * M), so that the
+    timed launches have the same append/merge mix as the headline's."""
+    import torch
+    K = -(-K // (R * w.M)) * (R * w.M)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    inp = stage_inputs(w, pool, dt)
+    sts, base0, u_dev = make_states(w, R, dt)
+    gms, per_launch = run_graph(w, inp, sts, K, W)
+    for st in sts:
+        st.close()
+    del sts
+    bases = [base0.clone() for _ in range(R)]
+    ems = run_eager_graph(w, inp, bases, u_dev, K, W)
+    del bases, inp
+    torch.cuda.empty_cache()
+    achieved = per_launch / (gms * 1e-3) / 1e9
+    return dict(rotate_states=R, steps=K, value=round(w.BH / (gms * 1e-3), 1), ms_per_step=round(gms, 5),
+                achieved_GBs=round(achieved, 1), frac=round(achieved / PEAK_HBM_GBS, 4),
+                eager_ms_per_step=round(ems, 5), deltalog_speedup=round(ems / gms, 3))
+
+
 def pages_context(res):
     """DeltaLog's published figures (the gist.science technical summary,
     "Results"; the authors' abstract) with their hardware, as context rather
@@ -640,6 +666,11 @@ def main():
                                 deltalog_speedup=r["eager_same_gpu"]["deltalog_speedup"])
             log(f"{o.describe()}: {r['wall_ms'] / K * 1e3:.2f} us/step")
 
+    deep = None
+    if default_shape and not args.quick:
+        deep = deep_rotation(w, K, W, 24, pool)
+        log(f"{w.describe()} over 24 states: {deep['ms_per_step'] * 1e3:.2f} us/step")
+
     cpu = None
     if not args.no_cpu:
         log("timing the CPU oracle ...")
@@ -670,6 +701,7 @@ def main():
         "per_slot": res.get("per_slot"),
         "two_stage": res.get("two_stage"),
         "eager_same_gpu": res.get("eager_same_gpu"),
+        "deep_rotation": deep,
         "other_workloads": others or None,
         "pages_context": pages_context(res),
     }
