@@ -2,29 +2,35 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1] [--rotate R] ...
 
-One "step" is one DeltaLog decode step (dl_decode_step: one launch of the
-step kernel, which also folds the log into the base on every M-th step) for
-all B*H slot-heads of one state, with its inputs already resident in HBM.
-The timed steps are replayed from a HIP graph of whole merge cycles, as a
-decode loop runs on the GPU; the same steps as direct launches are reported
-beside them.
-The default workload is GDN B=64 H=32 d_k=d_v=128 M=8 with bf16 q/k/v and an
-fp32 state.  With --rotate R (default 4) the steps go round R independent
-states, as the layers of a model do, so the 512 MiB working set exceeds the
-256 MB Infinity Cache and the state streams from HBM as in serving; the
-single-state figure (cache-resident) is reported beside it.
+One bench step is one whole pass of the method's schedule over one batch:
+a merge cycle of M decode steps (M-1 append launches, then the merge launch,
+each a dl_decode_step over all B*H slot-heads of one state), with its inputs
+already resident in HBM.  K bench steps are therefore K*M launches holding
+exactly K merges, whatever K is, and the throughput counts every decode step
+of every slot-head: (token*head)/s = B*H*M*K / region time.
 
-Prints ONE JSON line with the throughput in (token*head)/s, the roofline of
-the step kernel (algorithmic bytes per launch / mean launch time measured
-with HIP events on the replay stream), the direct-launch, same-GPU eager,
-two-stage and per-slot figures, the other operators' workloads, and the fp64
-CPU oracle timed on a bounded sample.
+With --rotate R (default 4) the launches go round R independent states, one
+launch each in turn, as the layers of a model are stepped; the 512 MiB working
+set exceeds the 256 MB Infinity Cache, so the state streams from HBM as in
+serving.  A round of R*M launches is a whole merge cycle of every state.  The
+timed rounds are replayed from HIP graphs, one graph per window of the staged
+input pool so that the inputs keep walking the pool; K mod R further cycles
+run as direct launches, M back to back on one state.  The default workload is
+GDN B=64 H=32 d_k=d_v=128 M=8 with bf16 q/k/v and an fp32 state.
+
+Prints ONE JSON line: the throughput, the roofline of the step kernel
+(algorithmic bytes per launch, averaged over the merge cycle, / mean launch
+time measured with HIP events on the replay stream), the launches and merges
+timed, the direct-launch, same-GPU eager, two-stage and per-slot figures, the
+cache-resident and 24-state figures, the other operators' workloads, and the
+fp64 CPU oracle timed on a bounded sample.
 """
 from __future__ import annotations
 
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -38,6 +44,7 @@ METRIC = "state-update (token·head)/s + achieved HBM GB/s vs peak, GDN B=64 H=3
 PEAK_HBM_GBS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "recurrent_state_update_amd", "csrc", "dl_kernels.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "step_kernel_traffic.json")
+MAX_GRAPHS = 64  # input windows captured as separate graphs (beyond that, windows repeat)
 
 
 def log(*a):
@@ -68,6 +75,13 @@ def step_launch_bytes(w, n: int, merge: bool) -> int:
     else:
         per += dk * z["es"] + z["lsz"] + dv * z["bsz"]
     return per * w.BH
+
+
+def cycle_launch_bytes(w) -> float:
+    """Mean algorithmic bytes per launch over one merge cycle (log lengths
+    0..M-1, the last launch merging).  Equals the per-step traffic model
+    P(1 + 1/M) + E((M-1)/M + (M-1)/2) + I per slot-head (modelled_step_bytes)."""
+    return sum(step_launch_bytes(w, n, n + 1 == w.M) for n in range(w.M)) / w.M
 
 
 def eager_launch_bytes(w) -> int:
@@ -121,172 +135,194 @@ def _ptrs(inp, s):
     return g("q"), g("k"), g("v"), g("beta"), g("ld")
 
 
-# ------------------------------------------------------------------- timing --
-def run_deltalog(w, inp, sts, K: int, W: int, instrument: bool, path: str = "fused"):
-    """W warm-up + K timed steps on state i % R.  Returns wall ms and, when
-    instrumented, per-launch kernel ms as (ms, n, merge) for the step kernel
-    plus the ReplayPrep ms (two-stage path).  The timed loop passes raw device
-    addresses straight to the C ABI."""
+# ----------------------------------------------------------- launch order --
+def launch_order(K: int, R: int, M: int) -> list:
+    """State index of each of the K*M launches of K merge cycles: K // R
+    rounds in which the R states take one launch each in turn (each round a
+    whole merge cycle of every state), then K % R cycles of one state each, M
+    launches back to back.  Every state ends where it started: log empty."""
+    order = [j % R for j in range((K // R) * R * M)]
+    for c in range(K % R):
+        order += [c] * M
+    return order
+
+
+def launch_kinds(order: list, M: int) -> list:
+    """Log length before each launch of `order` (all states starting empty)
+    and whether the launch merges."""
+    cnt = {}
+    out = []
+    for s in order:
+        n = cnt.get(s, 0) % M
+        out.append((n, n + 1 == M))
+        cnt[s] = cnt.get(s, 0) + 1
+    return out
+
+
+def time_cycles(launch, R: int, M: int, pool: int, K: int, W: int, graphs: bool = True,
+                first_input: int = 0) -> float:
+    """Run W warm-up cycles (rounded up to whole rounds, and replaying every
+    graph at least once), then time K merge
+    cycles (K*M launches, launch_order) between two HIP events on the launch
+    stream.  launch(state, input_index, stream) issues one launch; launch j of
+    the sequence uses input (first_input + j) % pool.  With graphs, each round
+    of R*M launches is replayed from a HIP graph captured for its window of
+    inputs; the K % R trailing cycles run directly.  Returns ms per launch."""
     import torch
-    import recurrent_state_update_amd as rsu
+    RM = R * M
+    nwin = pool // math.gcd(RM, pool)
+    nwin = min(nwin, MAX_GRAPHS)
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
-    pool = inp["q"].shape[0]
-    R = len(sts)
-    ptrs = [_ptrs(inp, s) for s in range(pool)]
-    outs = [torch.empty(w.B, w.H, w.dv, device="cuda") for _ in range(2)]
-    optr = [o.data_ptr() for o in outs]
+
+    def direct_round(win):
+        base = first_input + win * RM
+        for j in range(RM):
+            launch(j % R, (base + j) % pool, sp)
+
+    gs = []
+    if graphs:
+        torch.cuda.synchronize()
+        for win in range(nwin):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                csp = torch.cuda.current_stream().cuda_stream
+                base = first_input + win * RM
+                for j in range(RM):
+                    launch(j % R, (base + j) % pool, csp)
+            gs.append(g)
+
+    def round_(win):
+        if graphs:
+            gs[win % nwin].replay()
+        else:
+            direct_round(win % nwin)
+
+    # warm-up: W cycles rounded up to whole rounds, and at least one replay
+    # of every graph (a graph's first replay carries one-time setup)
+    warm = max(1, -(-W // R), nwin if graphs else 0)
+    for r in range(warm):
+        round_(r)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for r in range(K // R):
+        round_(warm + r)
+    j0 = first_input + (warm + K // R) * RM
+    for c in range(K % R):  # trailing cycles: M launches back to back on state c
+        for m in range(M):
+            launch(c, (j0 + c * M + m) % pool, sp)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / (K * M)
+
+
+def time_launches_bracketed(launch, R: int, M: int, pool: int, K: int, W: int) -> list:
+    """The same sequence as direct launches, each bracketed by its own pair of
+    HIP events (which adds event overhead to every launch).  Returns
+    [(ms, log length before, merges)] for the K*M launches."""
+    import torch
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    for j in range(max(1, -(-W // R)) * R * M):
+        launch(j % R, j % pool, sp)
+    order = launch_order(K, R, M)
+    kinds = launch_kinds(order, M)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in order]
+    torch.cuda.synchronize()
+    for j, s in enumerate(order):
+        evs[j][0].record(stream)
+        launch(s, j % pool, sp)
+        evs[j][1].record(stream)
+    torch.cuda.synchronize()
+    return [(a.elapsed_time(b), n, mg) for (a, b), (n, mg) in zip(evs, kinds)]
+
+
+# ------------------------------------------------------------------- paths --
+def deltalog_launcher(w, inp, sts, o):
+    import recurrent_state_update_amd as rsu
+    ptrs = [_ptrs(inp, s) for s in range(inp["q"].shape[0])]
+    hs = [st._h for st in sts]
+    f = rsu._lib.dl_decode_step
+    optr = o.data_ptr()
+
+    def launch(state, i, sp):
+        q, k, v, beta, ld = ptrs[i]
+        if f(hs[state], q, k, v, beta, ld, optr, sp) != 0:
+            raise RuntimeError("dl_decode_step failed")
+    return launch
+
+
+def staged_launcher(w, inp, sts, o):
+    """The two-stage path: dl_replay_prep then dl_append_decode."""
+    import recurrent_state_update_amd as rsu
+    ptrs = [_ptrs(inp, s) for s in range(inp["q"].shape[0])]
     hs = [st._h for st in sts]
     L = rsu._lib
+    optr = o.data_ptr()
 
-    def one(i, evs=None):
-        h = hs[i % R]
-        q, k, v, beta, ld = ptrs[i % pool]
-        if path == "fused":
-            if evs is not None:
-                evs[0].record(stream)
-            st = L.dl_decode_step(h, q, k, v, beta, ld, optr[i % 2], sp)
-            if evs is not None:
-                evs[1].record(stream)
-        else:
-            if evs is not None:
-                evs[0].record(stream)
-            st = L.dl_replay_prep(h, q, k, ld, sp)
-            if evs is not None:
-                evs[2].record(stream)
-            st = st or L.dl_append_decode(h, q, k, v, beta, optr[i % 2], sp)
-            if evs is not None:
-                evs[1].record(stream)
-        if st != 0:
-            raise RuntimeError(f"DeltaLog step failed: {rsu.dl_status_string(st)}")
-
-    for i in range(W):
-        one(i)
-    nev = 3 if path != "fused" else 2
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(K)] if instrument else None
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    ns = []
-    torch.cuda.synchronize()
-    t0.record(stream)
-    for i in range(K):
-        if instrument:
-            ns.append(sts[(W + i) % R].log_len)
-        one(W + i, evs[i] if instrument else None)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    wall = t0.elapsed_time(t1)
-    launches, prep = [], []
-    if instrument:
-        for i in range(K):
-            merge = ns[i] + 1 == w.M
-            if path == "fused":
-                launches.append((evs[i][0].elapsed_time(evs[i][1]), ns[i], merge))
-            else:
-                launches.append((evs[i][2].elapsed_time(evs[i][1]), ns[i], merge))
-                prep.append(evs[i][0].elapsed_time(evs[i][2]))
-    return wall, launches, prep
+    def launch(state, i, sp):
+        q, k, v, beta, ld = ptrs[i]
+        if L.dl_replay_prep(hs[state], q, k, ld, sp) != 0 or \
+                L.dl_append_decode(hs[state], q, k, v, beta, optr, sp) != 0:
+            raise RuntimeError("two-stage DeltaLog step failed")
+    return launch
 
 
-def graph_len(period: int, pool: int, K: int) -> int:
-    """Launches per captured graph: whole schedule periods that also walk the
-    whole input pool when that fits K whole times, else one period."""
-    import math
-    full = period * pool // math.gcd(period, pool)
-    return full if K % full == 0 else period
-
-
-def time_graph(launch, G: int, K: int, W: int) -> float:
-    """Capture launch(0..G-1) as one HIP graph and replay it ceil(W/G) times
-    untimed.  Then, between two HIP events on the replay stream, replay it
-    K // G times and issue the remaining K % G launches directly (continuing
-    the same sequence), so that exactly K launches are timed.  Returns ms per
-    launch."""
+def time_staged_bracketed(w, inp, sts, o, R: int, M: int, pool: int, K: int, W: int):
+    """The two-stage path as direct launches in launch_order, with events
+    before ReplayPrep, between the stages and after AppendDecode.  Returns the
+    mean ms of each stage (each bracket adds event overhead)."""
     import torch
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        sp = torch.cuda.current_stream().cuda_stream
-        for i in range(G):
-            launch(i, sp)
-    for _ in range(max(1, -(-W // G))):
-        g.replay()
-    torch.cuda.synchronize()
+    import recurrent_state_update_amd as rsu
+    ptrs = [_ptrs(inp, s) for s in range(pool)]
+    hs = [st._h for st in sts]
+    L = rsu._lib
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for _ in range(K // G):
-        g.replay()
-    for i in range(K % G):
-        launch(i, sp)
-    t1.record(stream)
+    launch = staged_launcher(w, inp, sts, o)
+    for j in range(max(1, -(-W // R)) * R * M):
+        launch(j % R, j % pool, sp)
+    order = launch_order(K, R, M)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in order]
     torch.cuda.synchronize()
-    return t0.elapsed_time(t1) / K
+    for j, s in enumerate(order):
+        q, k, v, beta, ld = ptrs[j % pool]
+        evs[j][0].record(stream)
+        st = L.dl_replay_prep(hs[s], q, k, ld, sp)
+        evs[j][1].record(stream)
+        if st != 0 or L.dl_append_decode(hs[s], q, k, v, beta, o.data_ptr(), sp) != 0:
+            raise RuntimeError("two-stage DeltaLog step failed")
+        evs[j][2].record(stream)
+    torch.cuda.synchronize()
+    n = len(order)
+    return (sum(e[0].elapsed_time(e[1]) for e in evs) / n, sum(e[1].elapsed_time(e[2]) for e in evs) / n)
 
 
-def run_graph(w, inp, sts, K: int, W: int):
-    """DeltaLog steps replayed from a HIP graph: G launches (state i % R,
-    inputs i % pool; whole merge cycles of every state) captured once and
-    replayed, any remainder of K launched directly.  Every state starts from
-    an empty log.  Returns (ms per step, mean algorithmic bytes per launch of
-    the K timed steps)."""
+def eager_launcher(w, inp, bases, u_dev, o):
     import recurrent_state_update_amd as rsu
-    import torch
-    R = len(sts)
-    pool = inp["q"].shape[0]
-    ptrs = [_ptrs(inp, s) for s in range(pool)]
-    o = torch.empty(w.B, w.H, w.dv, device="cuda")
-    for st in sts:
-        st.merge()
-    hs = [st._h for st in sts]
-
-    def launch(i, sp):
-        q, k, v, beta, ld = ptrs[i % pool]
-        if rsu._lib.dl_decode_step(hs[i % R], q, k, v, beta, ld, o.data_ptr(), sp) != 0:
-            raise RuntimeError("dl_decode_step failed")
-
-    G = graph_len(R * w.M, pool, K)
-    ms = time_graph(launch, G, K, W)
-    # bytes: whole cycles at the cycle mean; the remainder launch i steps
-    # state i % R at log length (i // R) mod M
-    rem = K % G
-    tot = (K - rem) * cycle_launch_bytes(w)
-    for i in range(rem):
-        n = (i // R) % w.M
-        tot += step_launch_bytes(w, n, n + 1 == w.M)
-    return ms, tot / K
-
-
-def run_eager_graph(w, inp, bases, u_dev, K: int, W: int):
-    """The eager step on R dense states, replayed from a HIP graph the same
-    way.  Returns ms per step."""
-    import recurrent_state_update_amd as rsu
-    import torch
-    R = len(bases)
-    pool = inp["q"].shape[0]
-    ptrs = [_ptrs(inp, s) for s in range(pool)]
-    o = torch.empty(w.B, w.H, w.dv, device="cuda")
+    ptrs = [_ptrs(inp, s) for s in range(inp["q"].shape[0])]
     bptr = [b.data_ptr() for b in bases]
     uptr = None if u_dev is None else u_dev.data_ptr()
     opi, dti = rsu.OPS[w.op], rsu.DTYPES[inp["q"].dtype]
+    f = rsu._lib.dl_eager_step
+    optr = o.data_ptr()
 
-    def launch(i, sp):
-        q, k, v, beta, ld = ptrs[i % pool]
-        if rsu._lib.dl_eager_step(opi, w.B, w.H, w.dk, w.dv, dti, bptr[i % R], q, k, v, beta, ld,
-                                  uptr, o.data_ptr(), sp) != 0:
+    def launch(state, i, sp):
+        q, k, v, beta, ld = ptrs[i]
+        if f(opi, w.B, w.H, w.dk, w.dv, dti, bptr[state], q, k, v, beta, ld, uptr, optr, sp) != 0:
             raise RuntimeError("dl_eager_step failed")
-
-    return time_graph(launch, graph_len(R, pool, K), K, W)
+    return launch
 
 
 def run_per_slot(w, inp, R: int, K: int, W: int):
     """Continuous batching: R fresh states with per-slot logs, slot b admitted
-    at step b % M, so in steady state every launch merges the B/M slots whose
-    logs are full and appends for the rest.  Then the odd slots are released
-    (half-occupied batch) and the same K launches are timed again.  Returns
-    (wall ms, algorithmic bytes) of K launches, full and half occupied."""
+    at step b % M, so in steady state every launch merges the slots whose logs
+    are full and appends for the rest.  K*M direct launches are timed (state
+    j % R in turn), then the odd slots are released (half-occupied batch) and
+    the same launches are timed again.  Returns (ms, algorithmic bytes) of the
+    K*M launches, full and half occupied."""
     import torch
     import synth
     import recurrent_state_update_amd as rsu
@@ -299,95 +335,66 @@ def run_per_slot(w, inp, R: int, K: int, W: int):
     sp = stream.cuda_stream
     pool = inp["q"].shape[0]
     ptrs = [_ptrs(inp, s) for s in range(pool)]
-    o = torch.empty(w.B, w.H, w.dv, device="cuda")
+    o = torch.zeros(w.B, w.H, w.dv, device="cuda")
     L = rsu._lib
+    RM = R * w.M
     for st in sts:
         st.enable_slots()
+    pos = [0]  # launches issued so far: launch i steps state i % R with input i % pool
 
-    def one(i):
-        q, k, v, beta, ld = ptrs[i % pool]
-        if L.dl_decode_step(sts[i % R]._h, q, k, v, beta, ld, o.data_ptr(), sp) != 0:
-            raise RuntimeError("dl_decode_step failed on a per-slot state")
+    def run(count, count_bytes=None):
+        """Issue `count` launches; with count_bytes(b) -> bool, also sum the
+        algorithmic bytes of the slots it selects from the host mirror of
+        every slot's log length."""
+        ones = w.with_(B=1, H=w.H)
+        tot = 0
+        for _ in range(count):
+            i = pos[0]
+            st = sts[i % R]
+            if count_bytes is not None:
+                tot += sum(step_launch_bytes(ones, n, n + 1 == w.M)
+                           for n in (st.slot_log_len(b) for b in range(w.B) if count_bytes(b)))
+            q, k, v, beta, ld = ptrs[i % pool]
+            if L.dl_decode_step(st._h, q, k, v, beta, ld, o.data_ptr(), sp) != 0:
+                raise RuntimeError("dl_decode_step failed on a per-slot state")
+            pos[0] += 1
+        return tot
 
-    for i in range(R * w.M):            # stagger: slot b starts at step b % M
+    for i in range(RM):                 # stagger: slot b starts at step b % M
         if i % R == 0:
             for b in range(i // R, w.B, w.M):
                 for st in sts:
                     st.admit(b)
-        one(i)
-    for i in range(W):
-        one(R * w.M + i)
-    ones = w.with_(B=1, H=w.H)
-    nbytes = 0
-    for i in range(K):
-        st = sts[(R * w.M + W + i) % R]
-        if i < R * w.M:                 # the schedule repeats every R*M launches
-            nbytes += sum(step_launch_bytes(ones, n, n + 1 == w.M)
-                          for n in (st.slot_log_len(b) for b in range(w.B)))
-        one(R * w.M + W + i)
-    torch.cuda.synchronize()
-    cyc = min(K, R * w.M)
-    nbytes = nbytes * K / cyc
+        run(1)
+    nl = K * w.M
+    # Bytes of the timed launches: the same launches run untimed first.  The
+    # schedule returns to the same phase of every slot after any multiple of
+    # R*M launches, so padding to such a multiple before the timed pass makes
+    # it repeat the counted launches exactly.
+    nbytes = run(nl, lambda b: True)
+    run((-nl) % RM + -(-(W * w.M) // RM) * RM)
+
     def timed():
+        torch.cuda.synchronize()
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
         t0.record(stream)
-        for i in range(K):
-            one(i)
+        run(nl)
         t1.record(stream)
         torch.cuda.synchronize()
         return t0.elapsed_time(t1)
 
     wall = timed()
+    run((-nl) % RM)
     for st in sts:  # half of the requests finish: their slots are released
         for b in range(1, w.B, 2):
             st.release(b)
-    half_bytes = nbytes * (w.B // 2 + w.B % 2) / w.B  # the slots b % M are spread evenly
-    for i in range(W):
-        one(i)
+    half_bytes = run(nl, lambda b: b % 2 == 0)
+    run((-nl) % RM)
     wall_half = timed()
     for st in sts:
         st.close()
     return wall, nbytes, wall_half, half_bytes
-
-
-def run_eager(w, inp, bases, u_dev, K: int, W: int, instrument: bool):
-    import torch
-    import recurrent_state_update_amd as rsu
-    stream = torch.cuda.current_stream()
-    sp = stream.cuda_stream
-    pool = inp["q"].shape[0]
-    R = len(bases)
-    o = torch.empty(w.B, w.H, w.dv, device="cuda")
-    ptrs = [_ptrs(inp, s) for s in range(pool)]
-    bptr = [b.data_ptr() for b in bases]
-    uptr = None if u_dev is None else u_dev.data_ptr()
-    opi, dti = rsu.OPS[w.op], rsu.DTYPES[inp["q"].dtype]
-    f = rsu._lib.dl_eager_step
-
-    def one(i, evs=None):
-        q, k, v, beta, ld = ptrs[i % pool]
-        if evs is not None:
-            evs[0].record(stream)
-        if f(opi, w.B, w.H, w.dk, w.dv, dti, bptr[i % R], q, k, v, beta, ld, uptr,
-             o.data_ptr(), sp) != 0:
-            raise RuntimeError("dl_eager_step failed")
-        if evs is not None:
-            evs[1].record(stream)
-
-    for i in range(W):
-        one(i)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)] if instrument else None
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record(stream)
-    for i in range(K):
-        one(W + i, evs[i] if instrument else None)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    per = [evs[i][0].elapsed_time(evs[i][1]) for i in range(K)] if instrument else []
-    return t0.elapsed_time(t1), per
 
 
 def cpu_baseline(w, budget_s=(8.0, 5.0), pool: int = 32):
@@ -428,8 +435,9 @@ def cpu_baseline(w, budget_s=(8.0, 5.0), pool: int = 32):
 
 
 def measured_traffic():
-    """HBM bytes per launch of the step kernel from the committed rocprofv3
-    counter summary, if it was taken on the current kernel source."""
+    """HBM bytes per launch of the step kernel (mean over a merge cycle) from
+    the committed rocprofv3 counter summary, if it was taken on the current
+    kernel source."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -442,90 +450,77 @@ def measured_traffic():
     return t.get("hbm_bytes_per_launch")
 
 
-def cycle_launch_bytes(w) -> float:
-    """Mean algorithmic bytes per launch over one merge cycle (log lengths
-    0..M-1, the last launch merging)."""
-    return sum(step_launch_bytes(w, n, n + 1 == w.M) for n in range(w.M)) / w.M
-
-
 def bench_workload(w, K, W, R, pool, with_eager=True, with_staged=True, quick=False):
-    """Time workload w.  Headline: K steps replayed from a HIP graph of whole
-    merge cycles (the way a decode loop runs on the GPU), timed with HIP events
-    on the replay stream; K / region length is the step rate and region length
-    / K the mean launch duration of the step kernel (gaps included).  Beside it:
-    the same steps as K direct launches, a per-launch event-bracketed pass that
-    splits append and merge launches (each bracket adds event overhead), the
-    two-stage path, per-slot logs, and the eager step (graph-replayed too)."""
+    """Time workload w over K merge cycles (K*M launches; launch_order).
+    Headline: graph-replayed, timed with HIP events on the replay stream;
+    region length / (K*M) is the step kernel's mean launch duration (gaps
+    included).  Beside it: the same launches issued directly, a pass with
+    every launch bracketed by events (append and merge means), the two-stage
+    path, per-slot logs, and the eager step over the same number of launches
+    (graph-replayed too)."""
     import torch
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     inp = stage_inputs(w, pool, dt)
     sts, base0, u_dev = make_states(w, R, dt)
+    o = torch.empty(w.B, w.H, w.dv, device="cuda")
+    M = w.M
+    nl = K * M
     res = {}
-    gms, per_launch = run_graph(w, inp, sts, K, W)
-    res["wall_ms"] = gms * K
-    res["value"] = w.BH / (gms * 1e-3)
-    achieved = per_launch / (gms * 1e-3) / 1e9
+    launch = deltalog_launcher(w, inp, sts, o)
+    ms = time_cycles(launch, R, M, pool, K, W, graphs=True)
+    cyc_bytes = cycle_launch_bytes(w)
+    res["ms_per_launch"] = ms
+    res["value"] = w.BH / (ms * 1e-3)
+    achieved = cyc_bytes / (ms * 1e-3) / 1e9
     res["roofline"] = dict(
         bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
         frac=round(achieved / PEAK_HBM_GBS, 4), traffic=None,
         kernel="step_kernel, one-launch append/merge modes (dl_decode_step)",
-        avg_launch_us=round(gms * 1e3, 2), bytes_per_launch=int(per_launch))
-    res["modelled_step_GBs"] = round(modelled_step_bytes(w) / (gms * 1e-3) / 1e9, 1)
+        avg_launch_us=round(ms * 1e3, 2), bytes_per_launch=int(round(cyc_bytes)),
+        launches_timed=nl, merge_launches_timed=sum(mg for _, mg in launch_kinds(launch_order(K, R, M), M)))
+    res["modelled_step_GBs"] = round(modelled_step_bytes(w) / (ms * 1e-3) / 1e9, 1)
     if quick:  # counter runs: the headline and the eager baseline only
         with_staged = False
-    # the same steps as direct launches
-    for st in sts:
-        st.merge()
-    wall, _, _ = run_deltalog(w, inp, sts, K, W, instrument=False, path="fused")
-    # the direct loop steps state i % R from an empty log, W of them untimed
-    cnt = [0] * R
-    direct_tot = 0
-    for i in range(W + K):
-        n = cnt[i % R] % w.M
-        if i >= W:
-            direct_tot += step_launch_bytes(w, n, n + 1 == w.M)
-        cnt[i % R] += 1
-    direct_bytes = direct_tot / K
-    if quick:
-        launches = []
-    else:
-        _, launches, _ = run_deltalog(w, inp, sts, K, W, instrument=True, path="fused")
-    res["direct_launch"] = dict(value=round(w.BH * K / (wall * 1e-3), 1), ms_per_step=round(wall / K, 5),
-                                achieved_GBs=round(direct_bytes / (wall / K * 1e-3) / 1e9, 1))
-    if launches:  # not taken in quick runs
-        app = [x[0] for x in launches if not x[2]]
-        mer = [x[0] for x in launches if x[2]]
+    dms = time_cycles(launch, R, M, pool, K, W, graphs=False)
+    res["direct_launch"] = dict(value=round(w.BH / (dms * 1e-3), 1), us_per_launch=round(dms * 1e3, 3),
+                                achieved_GBs=round(cyc_bytes / (dms * 1e-3) / 1e9, 1))
+    if not quick:
+        br = time_launches_bracketed(launch, R, M, pool, K, W)
+        app = [x[0] for x in br if not x[2]]
+        mer = [x[0] for x in br if x[2]]
         res["roofline"]["event_bracketed_us"] = dict(append=round(1e3 * sum(app) / max(len(app), 1), 2),
                                                      merge=round(1e3 * sum(mer) / max(len(mer), 1), 2))
     if R > 1 and not quick:
-        one, _, _ = run_deltalog(w, inp, sts[:1], K, W, instrument=False)
-        res["single_state_value"] = round(w.BH * K / (one * 1e-3), 1)
+        one = deltalog_launcher(w, inp, sts[:1], o)
+        sms = time_cycles(one, 1, M, pool, K, W, graphs=True)
+        res["single_state_value"] = round(w.BH / (sms * 1e-3), 1)
     if not quick:
         pw, pbytes, hw, hbytes = run_per_slot(w, inp, R, K, W)
-        res["per_slot"] = dict(value=round(w.BH * K / (pw * 1e-3), 1), ms_per_step=round(pw / K, 5),
+        res["per_slot"] = dict(value=round(w.BH * nl / (pw * 1e-3), 1), us_per_launch=round(pw / nl * 1e3, 3),
                                achieved_GBs=round(pbytes / (pw * 1e-3) / 1e9, 1),
                                frac=round(pbytes / (pw * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                                launch="direct",
-                               half_released=dict(ms_per_step=round(hw / K, 5),
+                               half_released=dict(us_per_launch=round(hw / nl * 1e3, 3),
                                                   achieved_GBs=round(hbytes / (hw * 1e-3) / 1e9, 1)))
     if with_staged:
-        sw, _, _ = run_deltalog(w, inp, sts, K, W, instrument=False, path="staged")
-        _, sl, sp = run_deltalog(w, inp, sts, K, W, instrument=True, path="staged")
-        res["two_stage"] = dict(value=round(w.BH * K / (sw * 1e-3), 1), ms_per_step=round(sw / K, 5),
+        staged = staged_launcher(w, inp, sts, o)
+        sms = time_cycles(staged, R, M, pool, K, W, graphs=False)
+        prep, app = time_staged_bracketed(w, inp, sts, o, R, M, pool, K, W)
+        res["two_stage"] = dict(value=round(w.BH / (sms * 1e-3), 1), us_per_step=round(sms * 1e3, 3),
                                 launch="direct",
-                                event_bracketed_us=dict(
-                                    append_decode=round(1e3 * sum(x[0] for x in sl) / len(sl), 2),
-                                    replay_prep=round(1e3 * sum(sp) / len(sp), 2)))
+                                event_bracketed_us=dict(replay_prep=round(1e3 * prep, 2),
+                                                        append_decode=round(1e3 * app, 2)))
     if with_eager:
         bases = [base0.clone() for _ in range(R)]
-        ems = run_eager_graph(w, inp, bases, u_dev, K, W)
-        ew, _ = run_eager(w, inp, bases, u_dev, K, W, instrument=False)
+        el = eager_launcher(w, inp, bases, u_dev, o)
+        ems = time_cycles(el, R, M, pool, K, W, graphs=True)
+        edms = time_cycles(el, R, M, pool, K, W, graphs=False)
         res["eager_same_gpu"] = dict(
-            value=round(w.BH / (ems * 1e-3), 1), ms_per_step=round(ems, 5),
+            value=round(w.BH / (ems * 1e-3), 1), us_per_launch=round(ems * 1e3, 3),
             achieved_GBs=round(eager_launch_bytes(w) / (ems * 1e-3) / 1e9, 1),
-            deltalog_speedup=round(ems / gms, 3),
-            direct_launch_ms_per_step=round(ew / K, 5),
-            deltalog_speedup_direct=round(ew / wall, 3))
+            deltalog_speedup=round(ems / ms, 3),
+            direct_us_per_launch=round(edms * 1e3, 3),
+            deltalog_speedup_direct=round(edms / dms, 3))
     for st in sts:
         st.close()
     del inp, sts
@@ -534,37 +529,39 @@ def bench_workload(w, K, W, R, pool, with_eager=True, with_staged=True, quick=Fa
 
 
 def deep_rotation(w, K: int, W: int, R: int, pool: int) -> dict:
-    """The headline steps over R states instead of the default 4, as a deep
+    """The headline launches over R states instead of the default 4, as a deep
     model's many layers would step them: R x (state + log) far exceeds the
     Infinity Cache, so the log entries, like the state, come from HBM.
-    DeltaLog and eager, both graph-replayed, over a whole number of merge
-    cycles of every state (K rounded up to a multiple of R * M), so that the
-    timed launches have the same append/merge mix as the headline's."""
+    DeltaLog and eager, both graph-replayed, over ceil(K / R) whole rounds
+    (R*M launches each, a whole merge cycle of every state)."""
     import torch
-    K = -(-K // (R * w.M)) * (R * w.M)
+    K = -(-K // R) * R
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     inp = stage_inputs(w, pool, dt)
     sts, base0, u_dev = make_states(w, R, dt)
-    gms, per_launch = run_graph(w, inp, sts, K, W)
+    o = torch.empty(w.B, w.H, w.dv, device="cuda")
+    ms = time_cycles(deltalog_launcher(w, inp, sts, o), R, w.M, pool, K, W, graphs=True)
     for st in sts:
         st.close()
     del sts
     bases = [base0.clone() for _ in range(R)]
-    ems = run_eager_graph(w, inp, bases, u_dev, K, W)
+    ems = time_cycles(eager_launcher(w, inp, bases, u_dev, o), R, w.M, pool, K, W, graphs=True)
     del bases, inp
     torch.cuda.empty_cache()
-    achieved = per_launch / (gms * 1e-3) / 1e9
-    return dict(rotate_states=R, steps=K, value=round(w.BH / (gms * 1e-3), 1), ms_per_step=round(gms, 5),
-                achieved_GBs=round(achieved, 1), frac=round(achieved / PEAK_HBM_GBS, 4),
-                eager_ms_per_step=round(ems, 5), deltalog_speedup=round(ems / gms, 3))
+    achieved = cycle_launch_bytes(w) / (ms * 1e-3) / 1e9
+    return dict(rotate_states=R, merge_cycles=K, launches=K * w.M, value=round(w.BH / (ms * 1e-3), 1),
+                us_per_launch=round(ms * 1e3, 3), achieved_GBs=round(achieved, 1),
+                frac=round(achieved / PEAK_HBM_GBS, 4), eager_us_per_launch=round(ems * 1e3, 3),
+                deltalog_speedup=round(ems / ms, 3))
 
 
 def pages_context(res):
     """DeltaLog's published figures (the gist.science technical summary,
     "Results"; the authors' abstract) with their hardware, as context rather
     than a target, beside this run's comparable ones: the kernel speedup over
-    the eager step on this GPU, and the state-write cut from the committed
-    counter summary when it was taken on the current kernel source."""
+    the eager step on this GPU (both over whole merge cycles), and the
+    state-write cut from the committed counter summary when it was taken on
+    the current kernel source."""
     cut = None
     try:
         with open(TRAFFIC_FILE) as f:
@@ -589,8 +586,8 @@ def pages_context(res):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=512)
-    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--steps", type=int, default=64, help="merge cycles timed (M launches each)")
+    ap.add_argument("--warmup", type=int, default=8, help="untimed merge cycles")
     ap.add_argument("--workload", type=int, default=1, choices=[1, 2, 3, 4])
     ap.add_argument("--op", default=None, help="operator of workload 4 (gdn|kda)")
     ap.add_argument("--M", type=int, default=None, help="merge interval (workload 4 sweep)")
@@ -611,6 +608,9 @@ def main():
         print("bench.py measures one GPU: the DeltaLog decode step needs no exchange between "
               "GPUs (slot-heads shard with zero communication), so there is no multi-GPU "
               "figure to take; run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -650,32 +650,33 @@ def main():
     pool = args.pool or min(w.steps, 256 if w.B <= 128 else 64)
     res = bench_workload(w, K, W, R, pool, quick=args.quick)
     default_shape = args.workload == 1 and not args.M and not args.B and not args.H
-    traffic = measured_traffic() if default_shape else None
-    res["roofline"]["traffic"] = traffic
-    log(f"{w.describe()}: {res['wall_ms'] / K * 1e3:.2f} us/step")
+    res["roofline"]["traffic"] = measured_traffic() if default_shape else None
+    log(f"{w.describe()}: {res['ms_per_launch'] * 1e3:.2f} us per decode step "
+        f"({K} merge cycles, {K * w.M} launches)")
 
     others = {}
     if not args.no_others and default_shape:
         for wid in (2, 3):
-            o = synth.WORKLOADS[wid]
-            r = bench_workload(o, K, W, R, min(o.steps, 256), with_staged=False)
-            others[o.op] = dict(workload=o.describe(), value=round(r["value"], 1),
-                                ms_per_step=round(r["wall_ms"] / K, 5),
-                                achieved_GBs=r["roofline"]["achieved"], frac=r["roofline"]["frac"],
-                                eager_value=r["eager_same_gpu"]["value"],
-                                deltalog_speedup=r["eager_same_gpu"]["deltalog_speedup"])
-            log(f"{o.describe()}: {r['wall_ms'] / K * 1e3:.2f} us/step")
+            ow = synth.WORKLOADS[wid]
+            r = bench_workload(ow, K, W, R, min(ow.steps, 256), with_staged=False)
+            others[ow.op] = dict(workload=ow.describe(), value=round(r["value"], 1),
+                                 us_per_launch=round(r["ms_per_launch"] * 1e3, 3),
+                                 achieved_GBs=r["roofline"]["achieved"], frac=r["roofline"]["frac"],
+                                 eager_value=r["eager_same_gpu"]["value"],
+                                 deltalog_speedup=r["eager_same_gpu"]["deltalog_speedup"])
+            log(f"{ow.describe()}: {r['ms_per_launch'] * 1e3:.2f} us per decode step")
 
     deep = None
     if default_shape and not args.quick:
         deep = deep_rotation(w, K, W, 24, pool)
-        log(f"{w.describe()} over 24 states: {deep['ms_per_step'] * 1e3:.2f} us/step")
+        log(f"{w.describe()} over 24 states: {deep['us_per_launch']:.2f} us per decode step")
 
     cpu = None
     if not args.no_cpu:
         log("timing the CPU oracle ...")
         cpu = cpu_baseline(w)
 
+    ms_launch = res["ms_per_launch"]
     out = {
         "metric": METRIC,
         "value": round(res["value"], 1),
@@ -683,16 +684,18 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": W,
-        "ms_per_step": round(res["wall_ms"] / K, 5),
+        "ms_per_step": round(ms_launch * w.M, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic (seeded PCG64; bf16 q/k/v, fp32 state, beta and log-decay)",
-        "config": {"workload": f"DeltaLog {w.op.upper()} decode step, B={w.B} H={w.H} "
-                               f"d_k={w.dk} d_v={w.dv} M={w.M}, {R} states stepped in turn",
+        "config": {"workload": f"DeltaLog {w.op.upper()} decode, B={w.B} H={w.H} d_k={w.dk} "
+                               f"d_v={w.dv} M={w.M}; one step = one merge cycle ({w.M} decode steps: "
+                               f"{w.M - 1} appends + 1 merge) of one state; {R} states stepped in turn",
                    "B": w.B, "H": w.H, "d_k": w.dk, "d_v": w.dv, "M": w.M, "op": w.op,
-                   "rotate_states": R, "input_pool_steps": pool},
+                   "decode_steps_per_step": w.M, "rotate_states": R, "input_pool_steps": pool},
+        "us_per_decode_step": round(ms_launch * 1e3, 3),
         "roofline": res["roofline"],
         "cpu_baseline": cpu,
         "modelled_step_GBs": res["modelled_step_GBs"],
