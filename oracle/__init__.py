@@ -59,8 +59,6 @@ class Oracle:
         args_step = [ctypes.c_int] * 5 + [_dp] * 8
         lib.orc_eager_step.argtypes = args_step
         lib.orc_eager_step.restype = None
-        lib.orc_eager_run.argtypes = [ctypes.c_int] * 6 + [_dp] * 8
-        lib.orc_eager_run.restype = None
         lib.orc_dl_step.argtypes = [ctypes.c_int] * 7 + [_dp] * 11
         lib.orc_dl_step.restype = ctypes.c_int
         lib.orc_dl_merge.argtypes = [ctypes.c_int] * 6 + [_dp] * 4
@@ -87,16 +85,6 @@ class Oracle:
         o = np.empty((B, H, dv), np.float64)
         self.lib.orc_eager_step(OP_IDS[op], B, H, dk, dv, _ptr(X), _ptr(q), _ptr(k),
                                 _ptr(v), _ptr(beta), _ptr(ld), _ptr(u), _ptr(o))
-        return o
-
-    def eager_run(self, op, X, q, k, v, beta, ld, u=None):
-        """T eager steps; inputs carry a leading step axis.  Returns o [T,B,H,dv]."""
-        B, H, dk, dv = X.shape
-        T = q.shape[0]
-        q, k, v, beta, ld, u = map(_f64, (q, k, v, beta, ld, u))
-        o = np.empty((T, B, H, dv), np.float64)
-        self.lib.orc_eager_run(OP_IDS[op], B, H, dk, dv, T, _ptr(X), _ptr(q), _ptr(k),
-                               _ptr(v), _ptr(beta), _ptr(ld), _ptr(u), _ptr(o))
         return o
 
 

@@ -162,24 +162,6 @@ void orc_eager_step(int op, int B, int H, int dk, int dv, double *X,
     }
 }
 
-/*
- * T consecutive eager steps: T calls of orc_eager_step, with the per-step
- * inputs stacked on a leading step axis (q [T,B,H,dk] ...) and o receiving
- * [T,B,H,dv].
- */
-void orc_eager_run(int op, int B, int H, int dk, int dv, int T, double *X,
-                   const double *q, const double *k, const double *v,
-                   const double *beta, const double *ld, const double *u,
-                   double *o)
-{
-    long BH = (long)B * H;
-    long ldn = op == ORC_GDN ? BH : BH * dk; /* log-decay values per step */
-    for (long t = 0; t < T; ++t)
-        orc_eager_step(op, B, H, dk, dv, X, q + t * BH * dk, k + t * BH * dk,
-                       v + t * BH * dv, beta ? beta + t * BH : beta,
-                       ld + t * ldn, u, o + t * BH * dv);
-}
-
 /* ------------------------------------------------------- DeltaLog model -- */
 
 /*

@@ -227,6 +227,7 @@ class DeltaLogState:
         st, h = dl_state_create(B, H, d_k, d_v, M, opi, dti, base, self.workspace, u)
         _check(st, "dl_state_create")
         self._h = h
+        self._per_slot = False
 
     # validation of per-step tensors
     def _inputs(self, q, k, v, beta, log_decay, o):
@@ -240,19 +241,31 @@ class DeltaLogState:
         if log_decay is not None:
             _want(log_decay, "log_decay", torch.float32, (B, H) if self.op == "gdn" else (B, H, dk), dev)
         if o is None:
-            o = torch.empty(B, H, dv, dtype=torch.float32, device=dev)
+            # on a per-slot handle the workgroups of released slots store
+            # nothing, so their rows of o keep what the buffer held: zeros
+            o = (torch.zeros if self._per_slot else torch.empty)(B, H, dv, dtype=torch.float32, device=dev)
         _want(o, "o", torch.float32, (B, H, dv), dev)
         return o
 
-    def step(self, q, k, v, beta, log_decay, o=None, stream=None):
-        """One decode step; returns o_t [B,H,d_v] fp32."""
-        o = self._inputs(q, k, v, beta, log_decay, o)
+    def _log_decay(self, log_decay):
         _want(log_decay, "log_decay", torch.float32,
-              (self.B, self.H) if self.op == "gdn" else (self.B, self.H, self.d_k))
+              (self.B, self.H) if self.op == "gdn" else (self.B, self.H, self.d_k), self.base.device)
+
+    def step(self, q, k, v, beta, log_decay, o=None, stream=None):
+        """One decode step; returns o_t [B,H,d_v] fp32.  On a handle with
+        per-slot logs, the rows of released slots are left as ``o`` held them
+        (zeros when ``o`` is not given)."""
+        o = self._inputs(q, k, v, beta, log_decay, o)
+        self._log_decay(log_decay)
         _check(dl_decode_step(self._h, q, k, v, beta, log_decay, o, stream), "dl_decode_step")
         return o
 
     def replay_prep(self, q, k, log_decay, stream=None):
+        """Stage 1 of the two-stage step (append_decode is stage 2)."""
+        dev = self.base.device
+        _want(q, "q", self.dtype, (self.B, self.H, self.d_k), dev)
+        _want(k, "k", self.dtype, (self.B, self.H, self.d_k), dev)
+        self._log_decay(log_decay)
         _check(dl_replay_prep(self._h, q, k, log_decay, stream), "dl_replay_prep")
 
     def append_decode(self, q, k, v, beta, o=None, stream=None):
@@ -273,6 +286,7 @@ class DeltaLogState:
     # per-slot logs (continuous batching)
     def enable_slots(self, stream=None):
         _check(dl_state_enable_slots(self._h, stream), "dl_state_enable_slots")
+        self._per_slot = True
 
     def admit(self, slot: int, stream=None):
         """Start a new request in ``slot``: write its initial state into

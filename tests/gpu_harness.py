@@ -2,10 +2,11 @@
 on seeded synthetic workloads and the fp64 oracle on the same inputs, and
 compares them.
 
-Error metric: for each output tensor and step, max|x - ref| / max|ref| over
-the compared elements (the max-abs relative error; the pages' accuracy bar is
-a maximum output relative error below 5e-3, the "Numerical correctness" item
-of the gist.science summary's results).
+Error metric: for each output tensor and step, and for each slot-head on its
+own, max|x - ref| / max|ref| (the max-abs relative error of that slot-head's
+output or state), then the worst slot-head.  The pages' accuracy bar is a
+maximum output relative error below 5e-3 (the "Numerical correctness" item of
+the gist.science summary's results).
 """
 from __future__ import annotations
 
@@ -23,18 +24,32 @@ FP32_TOL = 2e-4
 
 
 def rel(x, ref) -> float:
-    """Max-abs relative error; inf where x holds a NaN or inf that the
-    reference does not (so running maxima, which skip NaN, cannot hide one)."""
+    """Max-abs relative error, normalised per unit: x and ref are [units, ...]
+    with the leading axis indexing the compared units (slot-heads, or slots),
+    and the result is the max over units of max|x_u - ref_u| / max|ref_u|.  A
+    unit whose reference is all zero is measured against the largest |ref| of
+    the whole array.  So a unit with small values (a state just wiped by a
+    full decay, say) is judged on its own scale, not hidden under a larger
+    neighbour's.  inf where x holds a NaN or inf that the reference does not
+    (so running maxima, which skip NaN, cannot hide one); non-finite
+    reference entries that x matches are left out."""
     x, ref = np.broadcast_arrays(np.asarray(x, np.float64), np.asarray(ref, np.float64))
     fin = np.isfinite(ref)
     if (np.isfinite(x) != fin).any():
         return float("inf")
-    if not fin.all():
-        x, ref = x[fin], ref[fin]
+    if x.ndim < 2:
+        x, ref, fin = x.reshape(1, -1), ref.reshape(1, -1), fin.reshape(1, -1)
+    x = x.reshape(x.shape[0], -1)
+    ref = ref.reshape(ref.shape[0], -1)
+    fin = fin.reshape(fin.shape[0], -1)
     if ref.size == 0:
         return 0.0
-    den = np.max(np.abs(ref))
-    return float(np.max(np.abs(x - ref)) / den) if den > 0 else float(np.max(np.abs(x - ref)))
+    diff = np.where(fin, np.abs(x - ref), 0.0)
+    mag = np.where(fin, np.abs(ref), 0.0)
+    den = mag.max(axis=1)
+    glob = den.max()
+    den = np.where(den > 0, den, glob if glob > 0 else 1.0)
+    return float(np.max(diff.max(axis=1) / den))
 
 
 def dev(a, dtype=torch.float32):

@@ -218,34 +218,15 @@ def test_checkpoint_restore_mid_cycle(op):
 @needs_gpu
 @pytest.mark.parametrize("wid", [1, 2, 3])
 def test_full_size_workloads(orc, wid):
-    """Workloads 1-3 at full size (B*H slot-heads, all 256 steps, the
-    one-launch path the benchmark times).  Slot-heads are independent, so the
-    oracle follows a deterministic sample of 48 of them (first and last
-    included): o every step and the base after every merge."""
+    """Workloads 1-3 at full size and length (all B*H slot-heads, all 256
+    steps, the one-launch path the benchmark times): every output at every
+    step and the whole base after every merge, against the oracle."""
     w = synth.WORKLOADS[wid]
-    idx = sample_slot_heads(w.BH, 48, seed=wid)
-    run = ParityRun(w, idx=idx, orc=orc)
+    run = ParityRun(w, orc=orc)
     for _ in range(w.steps):
         run.step()
     assert run.checked_S == w.steps // w.M
-    _report(run, f"w{wid} full size")
-    run.close()
-
-
-@needs_gpu
-@pytest.mark.parametrize("op", ["gdn", "kda"])
-@pytest.mark.parametrize("M", [1, 2, 4, 8, 16])
-def test_large_batch_sweep_sizes(orc, op, M):
-    """The large-batch sweep shape (B=256 H=32 d=128, 512 MiB state) at each
-    merge interval: 32 steps (whole cycles for every M), 32 sampled
-    slot-heads, then a forced merge."""
-    w = synth.sweep_workload(op, M, steps=32)
-    idx = sample_slot_heads(w.BH, 32, seed=M)
-    run = ParityRun(w, idx=idx, orc=orc)
-    for _ in range(w.steps):
-        run.step()
-    run.merge()
-    _report(run, f"{op} B=256 M={M}")
+    _report(run, f"w{wid} full size, all {w.BH} slot-heads")
     run.close()
 
 
@@ -360,12 +341,12 @@ def test_full_size_graph_replay(orc, wid):
     """The launch configuration the benchmark times: dl_decode_step at the
     workload's full size, one merge cycle captured in a HIP graph and replayed
     for two cycles with fresh inputs copied into the captured buffers.  Every
-    output and the base after each cycle are checked on 48 sampled slot-heads
+    output and the base after each cycle are checked on all B*H slot-heads
     against the oracle."""
     import recurrent_state_update_amd as rsu
     w = synth.WORKLOADS[wid]
     M = w.M
-    idx = sample_slot_heads(w.BH, 48, seed=wid)
+    idx = np.arange(w.BH)
     X0, u = synth.initial(w)
     dt = in_dtype(w)
     base = dev(X0)
@@ -526,16 +507,19 @@ def test_runs_are_bit_identical(op):
 
 @needs_gpu
 @pytest.mark.parametrize("op", ["gdn", "kda"])
-def test_large_batch_long_run(orc, op):
-    """The large-batch configuration at its full length: B=256 H=32 d=128
-    (512 MiB state), M=8, all 1024 decode steps (128 merges), inputs cycling
-    a staged pool of 64 steps as the benchmark does.  32 sampled slot-heads:
-    every output, and the base after every merge, against the oracle (no
-    drift over the run)."""
+@pytest.mark.parametrize("M", list(synth.SWEEP_MS))
+def test_large_batch_long_run(orc, op, M):
+    """The large-batch configuration at its full length, at every merge
+    interval of the sweep: B=256 H=32 d=128 (512 MiB state), all 1024 decode
+    steps (1024 / M merges), inputs cycling a staged pool of 64 steps as the
+    benchmark does.  32 sampled slot-heads (first and last included; slot-heads
+    are independent, so a subset is exact): every output, and the base after
+    every merge, against the oracle (no drift over the run).  A forced merge at
+    the end must leave the base as it is (the log is empty)."""
     import recurrent_state_update_amd as rsu
-    w = synth.sweep_workload(op, 8, steps=1024)
+    w = synth.sweep_workload(op, M, steps=1024)
     pool = 64
-    idx = sample_slot_heads(w.BH, 32, seed=41)
+    idx = sample_slot_heads(w.BH, 32, seed=41 + M)
     sel = torch.from_numpy(idx).cuda()
     X0, u = synth.initial(w)
     dt = in_dtype(w)
@@ -557,9 +541,13 @@ def test_large_batch_long_run(orc, op):
         if st.log_len == 0:
             merges += 1
             worst_S = max(worst_S, rel(base.reshape(w.BH, w.dk, w.dv)[sel].cpu().numpy(), X[0]))
-    print(f"[{op} B=256 M=8 1024 steps] worst o={worst_o:.2e} S={worst_S:.2e} merges {merges}", flush=True)
+    st.merge()
+    worst_S = max(worst_S, rel(base.reshape(w.BH, w.dk, w.dv)[sel].cpu().numpy(), X[0]))
+    print(f"[{op} B=256 M={M} 1024 steps] worst o={worst_o:.2e} S={worst_S:.2e} merges {merges}",
+          flush=True)
     st.close()
-    assert merges == 128
+    assert merges == w.steps // M
+    assert worst_o < PAGES_TOL and worst_S < PAGES_TOL
     assert worst_o < FP32_TOL and worst_S < FP32_TOL
 
 
