@@ -8,7 +8,7 @@
  * d_k x d_v fp32 state ("Problem" section: S_t is d_k x d_v, held as a
  * [B,H,d_k,d_v] tensor).  Eager decoding rewrites the whole state every token.
  * DeltaLog keeps a dense base S-bar plus a bounded log of compact factors
- * (a_t, b_t) and log-decay snapshots Lambda ("Core mechanism: Base + Log"):
+ * (a_t, b_t) and log-decay metadata Lambda ("Core mechanism: Base + Log"):
  * M-1 of every M steps only append to the log, the M-th merges the log into
  * S-bar with one dense write.  Outputs equal eager decoding's up to floating
  * point rounding (abstract: the model observes the same dense state).
@@ -25,8 +25,12 @@
  *
  * Log contents (the pages name a_t, b_t, Lambda without formulas; the reading
  * implemented here): a_t = k_t; b_t = the delta-rule b_t above (fp32), or v_t
- * for RWKV6 (input dtype); Lambda_t = cumulative log-decay since the last
- * merge.  Between steps the logical state is
+ * for RWKV6 (input dtype); and ell_t, the step's log-decay.  The pages'
+ * log-decay snapshot Lambda_t (the cumulative log-decay since the last merge)
+ * is the running sum of the logged ell's; keeping the terms rather than their
+ * running sum lets every decay factor be formed as a sum of consecutive
+ * terms, exact to a few ulps even after repeated full forgetting.  Between
+ * steps the logical state is
  *   X = e^{Lambda_n} (.)row S-bar + sum_{j<=n} (e^{Lambda_n - Lambda_j} (.) a_j) b_j^T.
  *
  * Memory layouts (all row-major, all device memory, all caller-owned):
@@ -36,7 +40,7 @@
  *   log_decay      GDN [B,H] fp32; KDA, RWKV6 [B,H,d_k] fp32 (natural log, <= 0).
  *                  -inf (full forgetting: the step erases the history) is
  *                  accepted.  Values below -112 act as -112, where e^ell is
- *                  already exactly 0 in fp32; this keeps the log's cumulative
+ *                  already exactly 0 in fp32; this keeps every sum of logged
  *                  decays finite.
  *   u              RWKV6 bonus [H,d_k] fp32 (NULL for GDN, KDA)
  *   o              [B,H,d_v] fp32, 16-byte aligned
@@ -83,18 +87,28 @@ typedef enum {
 typedef struct dl_state dl_state; /* opaque host-side handle */
 
 /* Bytes of device workspace a handle of this shape needs (0 if the arguments
- * are invalid). */
+ * are invalid): the bounded log, M entries of O(d_k + d_v) factors per
+ * slot-head ("Core mechanism: Base + Log": the log of compact factors and
+ * log-decay metadata), plus the two-stage path's coefficients and the
+ * per-slot phases. */
 size_t dl_workspace_bytes(int B, int H, int d_k, int d_v, int M, dl_op op, dl_dtype in_dtype);
 
-/* Create a handle over caller-owned device memory.  `base` holds the initial
- * state S-bar_0 [B,H,d_k,d_v] fp32 and is updated in place on merge steps;
- * `workspace` has dl_workspace_bytes() bytes; `u` is RWKV6's bonus [H,d_k]
- * (NULL otherwise).  The log starts empty.  *out receives the handle. */
+/* Create a handle over caller-owned device memory ("Problem": one d_k x d_v
+ * state per slot and head, a [B,H,d_k,d_v] tensor; "Core mechanism: Base +
+ * Log": that tensor becomes the dense base S-bar, beside a bounded log).
+ * `base` holds the initial state S-bar_0 [B,H,d_k,d_v] fp32 and is updated
+ * in place on merge steps; `workspace` has dl_workspace_bytes() bytes; `u`
+ * is RWKV6's bonus [H,d_k] (NULL otherwise).  The log starts empty.  *out
+ * receives the handle.  Errors: DL_E_INVALID (null or overlapping buffers,
+ * B/H/M out of range, u missing for RWKV6), DL_E_SHAPE, DL_E_ALIGN. */
 dl_status dl_state_create(int B, int H, int d_k, int d_v, int M, dl_op op, dl_dtype in_dtype,
                           float *base, void *workspace, const float *u, dl_state **out);
 
-/* One decode step for all B*H slot-heads (append phase, or the merge phase on
- * the step that brings the log to M entries).  Writes o_t [B,H,d_v] fp32.
+/* One decode step for all B*H slot-heads ("Core mechanism: Base + Log": the
+ * append phase, which writes only the step's compact factors and log-decay,
+ * on M-1 of every M steps; the merge phase, which folds the log into S-bar
+ * with one dense write and empties it, on the step that brings the log to M
+ * entries).  Writes o_t [B,H,d_v] fp32.
  * q is r for RWKV6.  beta may be NULL for RWKV6.  One kernel launch: each
  * value-tile workgroup also does its slot-head's ReplayPrep work.  Computes
  * the same step as dl_replay_prep followed by dl_append_decode (the results
@@ -103,29 +117,37 @@ dl_status dl_decode_step(dl_state *s, const void *q, const void *k, const void *
                          const float *beta, const float *log_decay, float *o, void *stream);
 
 /* Stage 1 of a decode step ("Kernel implementation": the shared ReplayPrep
- * stage, once per slot-head): cumulative log-decay, replay coefficients of the
- * n pending entries against q_t and k_t, q.k (RWKV6: r.(u (.) k)), and the
- * key-side append (a = k, Lambda snapshot).  Must be followed by
- * dl_append_decode with the same q and k before any other call on s. */
+ * stage, once per slot-head): the replay coefficients of the n pending
+ * entries against q_t and k_t (their decay factors e^{Lambda' - Lambda_j}
+ * formed from the logged log-decays), q.k (RWKV6: r.(u (.) k)), and the
+ * key-side append (a = k and this step's log-decay).  Must be followed by
+ * dl_append_decode with the same q and k before any other call on s
+ * (otherwise DL_E_STATE). */
 dl_status dl_replay_prep(dl_state *s, const void *q, const void *k, const float *log_decay,
                          void *stream);
 
-/* Stage 2 of a decode step (AppendDecode, parallel over value tiles): streams
- * S-bar, adds the replayed log, writes o_t and the value-side factor b_t; on
- * the M-th step also folds the whole log into S-bar (one dense write). */
+/* Stage 2 of a decode step ("Kernel implementation": AppendDecode, parallel
+ * over value tiles, each owning a slice of S-bar and the matching value-side
+ * log shard): streams S-bar, adds the replayed log, writes o_t and the
+ * value-side factor b_t; on the M-th step also folds the whole log into S-bar
+ * (one dense write).  DL_E_STATE unless dl_replay_prep ran just before. */
 dl_status dl_append_decode(dl_state *s, const void *q, const void *k, const void *v,
                            const float *beta, float *o, void *stream);
 
-/* Merge now: fold the n pending entries into S-bar so that `base` holds the
- * logical state; empties the log.  No-op (DL_OK) when the log is empty. */
+/* Merge now ("Core mechanism: Base + Log", the merge phase, taken before its
+ * M-th step): fold the n pending entries into S-bar with one dense write so
+ * that `base` holds the logical state; empties the log.  No-op (DL_OK) when
+ * the log is empty.  DL_E_STATE between dl_replay_prep and
+ * dl_append_decode. */
 dl_status dl_merge(dl_state *s, void *stream);
 
 /* Empty the log without folding it (S-bar is left as is): drops the pending
  * updates.  For restarting a handle over a freshly written base. */
 dl_status dl_state_reset(dl_state *s);
 
-/* Number of pending log entries, 0..M-1 (-1 for a NULL handle or a handle
- * with per-slot logs: use dl_slot_log_len). */
+/* Number of pending log entries, 0..M-1 ("Core mechanism: Base + Log": the
+ * log is bounded, holding at most M-1 entries between steps); -1 for a NULL
+ * handle or a handle with per-slot logs (use dl_slot_log_len). */
 int dl_log_len(const dl_state *s);
 
 /* Set the number of pending entries to n (0..M-1) after the caller restored
@@ -133,12 +155,18 @@ int dl_log_len(const dl_state *s);
  * checkpoint/restore). */
 dl_status dl_set_log_len(dl_state *s, int n);
 
-/* Release the handle (not the caller's device memory).  NULL is accepted. */
+/* Release the handle (host memory; the caller's device buffers are left as
+ * they are, and the base holds S-bar, the logical state only if the log is
+ * empty: see dl_merge).  NULL is accepted. */
 dl_status dl_state_destroy(dl_state *s);
 
-/* The same-GPU baseline: one eager step that reads and rewrites the whole
- * state S [B,H,d_k,d_v] every token (the "dense recurrent" schedule the pages
- * compare against).  u is RWKV6's bonus [H,d_k]. */
+/* The same-GPU baseline ("Problem": eager decoding applies each token's update
+ * to the whole state and writes the full [B,H,d_k,d_v] tensor back to HBM on
+ * every step; the abstract's dense recurrent baselines): one eager step that
+ * reads and rewrites S [B,H,d_k,d_v] in place and writes o [B,H,d_v].  u is
+ * RWKV6's bonus [H,d_k] (NULL otherwise); beta may be NULL for RWKV6.
+ * Errors as for dl_decode_step, plus DL_E_INVALID if S overlaps another
+ * buffer. */
 dl_status dl_eager_step(dl_op op, int B, int H, int d_k, int d_v, dl_dtype in_dtype, float *S,
                         const void *q, const void *k, const void *v, const float *beta,
                         const float *log_decay, const float *u, float *o, void *stream);
@@ -196,7 +224,7 @@ dl_status dl_slot_release(dl_state *s, int slot, void *stream);
  * a released slot), -1 for a bad handle or slot. */
 int dl_slot_log_len(const dl_state *s, int slot);
 
-/* Static description of a status code. */
+/* Static description of a status code (never NULL; owned by the library). */
 const char *dl_status_string(dl_status st);
 
 #ifdef __cplusplus

@@ -11,9 +11,11 @@
 //
 // Notation (one slot-head): X-bar is the d_k x d_v fp32 base, row i = key i.
 // Log entry j < n holds a_j = k_j (input dtype), b_j (fp32 for the delta rule,
-// input dtype for RWKV6) and Lam_j, the cumulative log-decay since the last
-// merge (one float for GDN, d_k floats for KDA and RWKV6).  Lam' = Lam_{n-1} +
-// ell_t (Lam_{-1} = 0).  The logical state after entries 0..n-1 is
+// input dtype for RWKV6) and ell_j, the log-decay of the step that appended it
+// (one float for GDN, d_k floats for KDA and RWKV6).  The pages' log-decay
+// snapshot is their running sum Lam_j = ell_0 + ... + ell_j, the cumulative
+// log-decay since the last merge; Lam' = Lam_{n-1} + ell_t (Lam_{-1} = 0).
+// The logical state after entries 0..n-1 is
 //   X = e^{Lam_{n-1}} (.)row X-bar + sum_j (e^{Lam_{n-1} - Lam_j} (.) a_j) b_j^T.
 // Decayed state X' = D_t X, so for the delta rule
 //   X'^T k = X-bar^T (e^{Lam'} (.) k) + sum_j c^k_j b_j,
@@ -22,7 +24,10 @@
 // RWKV6 reads the state before the step: o_t = X-bar^T (e^{Lam_{n-1}} (.) r)
 // + sum_j c^r_j b_j + (r.(u (.) k)) v.  A merge folds entries to
 //   X-bar <- e^{Lam_f} (.)row X-bar + sum_j (e^{Lam_f - Lam_j} (.) a_j) b_j^T.
-// Only exponents <= 0 are ever taken (differences of cumulative log-decays).
+// Every exponent is a sum of consecutive ell's, Lam_{n-1} - Lam_j = ell_{j+1}
+// + ... + ell_{n-1}, formed by adding the logged ell's directly (suffix sums),
+// never as the difference of two cumulative values: all terms are <= 0, so
+// the sums are exact to a few ulps of their own size and exponents are <= 0.
 //
 // Hardware mapping.  The step is a matrix-vector product plus (on merges) a
 // rank-M update: ~1-2 flop per state byte, far under the fp32 balance, so it is
@@ -243,23 +248,35 @@ __host__ __device__ constexpr int fold_rows(int mode, int n)
 constexpr int kRowTables = 8;
 // Floats per row table: d_k entries and a pad slot, rounded to 16 bytes.
 __host__ __device__ constexpr int row_table_stride(int DK) { return DK + 4; }
-// Dynamic LDS floats of the step kernel: eight per-row tables [DK], Bt
-// [bt_rows][T], F [fold_rows][DK], coefficients [2n+1], then a 16-byte aligned
-// junk slot: lanes with nothing to publish store there, which keeps the
-// publishing stores unconditional.
-__host__ __device__ constexpr int dyn_floats(int mode, int n, int DK, int T)
+// Modes that read the log's decays: every mode but the eager step.
+__host__ __device__ constexpr bool mode_has_log(int mode) { return mode_logged(mode) || mode_fold(mode); }
+// Rows of the per-key table [rows][DK]: the fold rows of the merging modes,
+// and for a per-key decay (KDA, RWKV6) at least the n logged entries, whose
+// log-decays are staged there and turned into suffix sums in place (a fold
+// row m then overwrites suffix-sum row m).
+__host__ __device__ constexpr int key_rows(int op, int mode, int n)
 {
-    return kRowTables * row_table_stride(DK) + bt_rows(mode, n) * T + fold_rows(mode, n) * DK +
-           (mode_logged(mode) ? 2 * n + 1 : 0) + 3 + 4;
+    return (op != GDN && mode_has_log(mode) && n > fold_rows(mode, n)) ? n : fold_rows(mode, n);
+}
+// Dynamic LDS floats of the step kernel: eight per-row tables [DK], Bt
+// [bt_rows][T], the per-key table [key_rows][DK], coefficients [2n+1], GDN's
+// n suffix sums, then a 16-byte aligned junk slot: lanes with nothing to
+// publish store there, which keeps the publishing stores unconditional.
+__host__ __device__ constexpr int dyn_floats(int op, int mode, int n, int DK, int T)
+{
+    return kRowTables * row_table_stride(DK) + bt_rows(mode, n) * T + key_rows(op, mode, n) * DK +
+           (mode_logged(mode) ? 2 * n + 1 : 0) + (op == GDN && mode_has_log(mode) ? n : 0) + 3 + 4;
 }
 
 // ------------------------------------------------------------- ReplayPrep --
 //
 // One wave64 per slot-head, four slot-heads per workgroup.  Per slot-head:
-// Lam' = Lam_{n-1} + ell_t; coefficients c^q_j, c^k_j (RWKV6: c^r_j against
-// Lam_{n-1}) for the n logged entries; kappa = q.k (RWKV6: r.(u (.) k)); then
-// the key-side append a_n = k, Lam_n = Lam'.  coef row: [c^q_0..M-1,
-// c^k_0..M-1, kappa].
+// coefficients c^q_j, c^k_j (RWKV6: c^r_j) of the n logged entries, with the
+// factor e^{Lam' - Lam_j} (RWKV6: e^{Lam_{n-1} - Lam_j}) formed as e^{S_j +
+// ell_t} (RWKV6: e^{S_j}) from the suffix sum S_j of the logged log-decays
+// after entry j, accumulated newest entry first; kappa = q.k (RWKV6:
+// r.(u (.) k)); then the key-side append a_n = k, ell_n = ell_t.  coef row:
+// [c^q_0..M-1, c^k_0..M-1, kappa].
 template <int OP, typename TIn, int DK>
 __global__ __launch_bounds__(256) void replay_prep_kernel(StepArgs a)
 {
@@ -275,46 +292,50 @@ __global__ __launch_bounds__(256) void replay_prep_kernel(StepArgs a)
     const rsrc_t ar = make_rsrc(static_cast<const TIn *>(a.alog) + (long)sh * M * DK, n * DK * sizeof(TIn));
     const rsrc_t lr = make_rsrc(L, (OP == GDN ? n : n * DK) * 4);
 
+    // batch b holds entries top - e, e < EB, top = n - 1 - b EB (newest first)
     float am[EB][KPL], lm[EB][KPL], gm[EB];
-    auto load_batch = [&](int m0) {
+    auto load_batch = [&](int top) {
 #pragma unroll
         for (int e = 0; e < EB; ++e) {
-            const int m = m0 + e;
-            gm[e] = OP == GDN ? buf_ldf(lr, m < n ? (unsigned)m * 4u : kSkip) : 0.f;
+            const int m = top - e;
+            gm[e] = OP == GDN ? buf_ldf(lr, m >= 0 ? (unsigned)m * 4u : kSkip) : 0.f;
 #pragma unroll
             for (int c = 0; c < KPL; ++c) {
                 const int i = lane + 64 * c;
-                const unsigned ei = (m < n && i < DK) ? (unsigned)(m * DK + i) : kSkipElem;
+                const unsigned ei = (m >= 0 && i < DK) ? (unsigned)(m * DK + i) : kSkipElem;
                 am[e][c] = buf_ld_in<TIn>(ar, ei);
                 lm[e][c] = OP != GDN ? buf_ld_in<float>(lr, ei) : 0.f;
             }
         }
     };
-    load_batch(0); // first batch of entry loads, ahead of everything else
+    load_batch(n - 1); // first batch of entry loads, ahead of everything else
     const rsrc_t qr = make_rsrc(static_cast<const TIn *>(a.q) + (long)sh * DK, DK * sizeof(TIn));
     const rsrc_t kr = make_rsrc(static_cast<const TIn *>(a.k) + (long)sh * DK, DK * sizeof(TIn));
-    float qv[KPL], kv[KPL], lp[KPL], lw[KPL];
+    float qv[KPL], kv[KPL], ell[KPL], sfx[KPL];
 #pragma unroll
     for (int c = 0; c < KPL; ++c) {
         const int i = lane + 64 * c;
         const unsigned ei = i < DK ? (unsigned)i : kSkipElem;
         qv[c] = buf_ld_in<TIn>(qr, ei);
         kv[c] = buf_ld_in<TIn>(kr, ei);
-        // Lam_{n-1} is entry n-1 of the log (0 when the log is empty)
-        lp[c] = OP == GDN ? (n > 0 ? buf_ldf(lr, (unsigned)(n - 1) * 4u) : 0.f)
-                          : buf_ld_in<float>(lr, (n > 0 && i < DK) ? (unsigned)((n - 1) * DK + i) : kSkipElem);
-        lw[c] = lp[c] + floor_log_decay(OP == GDN ? a.ld[sh] : (i < DK ? a.ld[(long)sh * DK + i] : 0.f));
+        ell[c] = floor_log_decay(OP == GDN ? a.ld[sh] : (i < DK ? a.ld[(long)sh * DK + i] : 0.f));
+        sfx[c] = 0.f; // running suffix sum of the logged per-key log-decays
     }
+    float gsfx = 0.f; // GDN: the same for its scalar log-decays
 
     float *coef = a.coef + (long)sh * a.cstride;
-    for (int m0 = 0; m0 < n; m0 += EB) {
-        if (m0 > 0)
-            load_batch(m0);
+    for (int top = n - 1; top >= 0; top -= EB) {
+        if (top < n - 1)
+            load_batch(top);
 #pragma unroll
         for (int e = 0; e < EB; ++e) {
-            const int m = m0 + e;
-            if (m >= n)
+            const int m = top - e;
+            if (m < 0)
                 break; // uniform over the wave
+            // GDN: the entry's scalar factor e^{S_m + ell_t}, applied after the sum
+            const float g = OP == GDN ? expf(gsfx + ell[0]) : 1.f;
+            if (OP == GDN)
+                gsfx += gm[e];
             float sq = 0.f, sk = 0.f;
 #pragma unroll
             for (int c = 0; c < KPL; ++c) {
@@ -322,22 +343,21 @@ __global__ __launch_bounds__(256) void replay_prep_kernel(StepArgs a)
                     continue;
                 float f;
                 if (OP == GDN)
-                    f = am[e][c]; // scalar decay factor applied after the sum
+                    f = am[e][c];
                 else if (OP == KDA)
-                    f = expf(lw[c] - lm[e][c]) * am[e][c];
+                    f = expf(sfx[c] + ell[c]) * am[e][c];
                 else
-                    f = expf(lp[c] - lm[e][c]) * am[e][c];
+                    f = expf(sfx[c]) * am[e][c];
                 sq = fmaf(f, qv[c], sq);
                 sk = fmaf(f, kv[c], sk);
+                if (OP != GDN)
+                    sfx[c] += lm[e][c];
             }
             sq = wave_sum_from<1>(sq);
             if (OP != RWKV6)
                 sk = wave_sum_from<1>(sk);
-            if (OP == GDN) {
-                const float g = expf(lw[0] - gm[e]);
-                sq *= g;
-                sk *= g;
-            }
+            sq *= g;
+            sk *= g;
             if (lane == 0) {
                 coef[m] = sq;
                 if (OP != RWKV6)
@@ -365,11 +385,19 @@ __global__ __launch_bounds__(256) void replay_prep_kernel(StepArgs a)
         if (i < DK) {
             an[i] = to_in<TIn>(kv[c]);
             if (OP != GDN)
-                L[(long)n * DK + i] = lw[c];
+                L[(long)n * DK + i] = ell[c];
         }
     }
     if (OP == GDN && lane == 0)
-        L[n] = lw[0];
+        L[n] = ell[0];
+}
+
+// Waves per SIMD the compiler must leave room for: 8 (64 VGPRs) for the
+// per-slot step with bf16 inputs, which fits them with no spill but left to
+// itself takes a few more and drops to 7; the compiler's own choice elsewhere.
+template <typename TIn> __host__ __device__ constexpr int min_waves(int mode)
+{
+    return (mode == SSTEP && sizeof(TIn) == 2) ? 8 : 1;
 }
 
 // -------------------------------------------------------------- step kernel --
@@ -391,7 +419,8 @@ __global__ __launch_bounds__(256) void replay_prep_kernel(StepArgs a)
 //                    merge workgroups.
 // Merging launches end with the fold and the single dense write.
 template <int OP, typename TIn, int DK, int DV, int MODE>
-__global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
+__global__ __launch_bounds__((TileCfg<DK, DV>::NT)) __attribute__((amdgpu_waves_per_eu(min_waves<TIn>(MODE))))
+void step_kernel(StepArgs a)
 {
     using C = TileCfg<DK, DV>;
     constexpr int T = C::T, NT = C::NT, LPR = C::LPR, RPP = C::RPP, P = C::P;
@@ -446,27 +475,43 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
 
     const int nb = bt_rows(MODE, n);
     const int nf = merging ? n + 1 : MODE == EAGER ? 1 : FOLDS ? n : 0;
+    // The log holds each entry's own step log-decay ell_j (floored); the
+    // cumulative Lam_j is their running sum.  Every factor a step needs is
+    // e^(a sum of consecutive ell's): with Lam_{n-1} = T = sum_j ell_j and
+    // S_m = sum_{j>m} ell_j, the base weights are e^(T + offset) and entry m's
+    // factors e^(S_m + offset), offset = ell_t or 0.  Summing the ell's
+    // directly (all <= 0) keeps these exact to a few ulps even after full
+    // forgetting: a wiped step (-112) makes every sum across it <= -112,
+    // whose exponential is 0, and no difference of two large cumulative
+    // values is ever formed.
+    constexpr bool KEYLOG = OP != GDN && mode_has_log(MODE); // per-key decays of logged entries
+    const bool scan = KEYLOG && n > 0;                       // uniform over the workgroup
+    const int kr = KEYLOG && n > nf ? n : nf;                // rows of the per-key table
     // Per-row tables, each TS = d_k + 4 floats: entry d_k is a pad slot that
     // lanes past d_k write to, so one row index addresses every table.
     constexpr int TS = row_table_stride(DK);
     float *Wq = dyn;             // read weights, q side
     float *Wk = dyn + TS;        // read weights, k side
     float *Rf = dyn + 2 * TS;    // fold base factor e^{Lam_f}
-    float *Lf = dyn + 3 * TS;    // fold log-decay Lam_f
+    float *Lf = dyn + 3 * TS;    // fold offset: Lam_f - Lam_{n-1}
     float *Qk = dyn + 4 * TS;    // q.k (RWKV6: r.(u (.) k)) terms
     float *Qr = dyn + 5 * TS;    // raw q (FUSED coefficient pass)
     float *Kr = dyn + 6 * TS;    // raw k (FUSED)
-    float *Lx = dyn + 7 * TS;    // replay log-decay: Lam' (delta) / Lam_{n-1} (RWKV6) (FUSED)
+    float *Lx = dyn + 7 * TS;    // read offset: Lam' - Lam_{n-1} (delta) / 0 (RWKV6) (FUSED)
     float *Bt = dyn + kRowTables * TS;         // [nb][T] value-side factors of this tile
-    float *F = Bt + nb * T;                    // [nf][DK] key-side fold coefficients
-    float *cf = F + nf * DK;                   // [2n+1] c^q, c^k, kappa (LOGGED)
-    float *junk = dyn + ((kRowTables * TS + nb * T + nf * DK + (LOGGED ? 2 * n + 1 : 0) + 3) & ~3);
+    float *F = Bt + nb * T;                    // [kr][DK] per-key table: logged decays, turned
+                                               // into suffix sums in place, then fold rows
+    float *cf = F + kr * DK;                   // [2n+1] c^q, c^k, kappa (LOGGED)
+    float *gsum = cf + (LOGGED ? 2 * n + 1 : 0); // GDN: [n] suffix sums S_m
+    float *junk = dyn + ((kRowTables * TS + nb * T + kr * DK + (LOGGED ? 2 * n + 1 : 0) +
+                          (OP == GDN && mode_has_log(MODE) ? n : 0) + 3) & ~3);
 
     // ------------------------------------------------------ 0. small loads --
     // Row metadata for rows i = tid + j*NT (lanes past d_k skip).
     const rsrc_t q_r = make_rsrc(static_cast<const TIn *>(a.q) + (long)sh * DK, READS ? DK * ES : 0);
     const rsrc_t k_r = make_rsrc(static_cast<const TIn *>(a.k) + (long)sh * DK, READS ? DK * ES : 0);
-    // the Lambda log: Lam_{n-1} is entry n-1, Lam_n (from ReplayPrep) entry n
+    // the log-decay log: entry j's ell_j at [j] (GDN) or [j][DK]; entry n holds
+    // this step's, appended by ReplayPrep on the two-stage path
     const rsrc_t L_r = make_rsrc(L, MODE == EAGER ? 0 : (OP == GDN ? M : M * DK) * 4);
     const rsrc_t ld_r = make_rsrc(a.ld + (OP == GDN ? sh : (long)sh * DK),
                                   (MODE == EAGER || FUSED) ? (OP == GDN ? 1 : DK) * 4 : 0);
@@ -474,39 +519,50 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
     // Loads are skipped outright (wave-uniform branches) where a whole wave
     // needs none of them, and pointed past the resource end where only some
     // of its lanes do.
-    unsigned rq_[RW], rk_[RW], rprev[RW], rcur[RW], rell[RW], ru[RW]; // raw words
+    unsigned rq_[RW], rk_[RW], rell[RW], ru[RW]; // raw words
 #pragma unroll
     for (int j = 0; j < RW; ++j) {
         const int i = tid + j * NT;
         const unsigned ei = i < DK ? (unsigned)i : kSkipElem;
         // skipped loads leave an unused, non-constant placeholder (a constant
         // would let the compiler fold the later conversion into the branch)
-        rq_[j] = rk_[j] = rprev[j] = rcur[j] = rell[j] = ru[j] = (unsigned)tid;
+        rq_[j] = rk_[j] = rell[j] = ru[j] = (unsigned)tid;
         if (wave * 64 + j * NT < DK) { // this wave holds rows of the tables
             if (READS) {
                 rq_[j] = buf_raw1<TIn>(q_r, ei);
                 rk_[j] = buf_raw1<TIn>(k_r, ei);
             }
-            // per-key log-decays: Lam_{n-1} (0 when the log is empty), Lam_n, ell_t
+            // this step's per-key log-decay: the input, or entry n of the log
             if (OP != GDN) {
-                if (n > 0 && MODE != EAGER)
-                    rprev[j] = buf_raw1<float>(L_r, i < DK ? (unsigned)((n - 1) * DK + i) : kSkipElem);
                 if (STAGED)
-                    rcur[j] = buf_raw1<float>(L_r, i < DK ? (unsigned)(n * DK + i) : kSkipElem);
-                if (MODE == EAGER || FUSED)
+                    rell[j] = buf_raw1<float>(L_r, i < DK ? (unsigned)(n * DK + i) : kSkipElem);
+                else if (MODE == EAGER || FUSED)
                     rell[j] = buf_raw1<float>(ld_r, ei);
             }
             if (OP == RWKV6 && KAPPA_HERE)
                 ru[j] = buf_raw1<float>(u_r, ei);
         }
     }
-    // GDN: the head's scalar log-decays (wave-uniform)
-    float gprev = 0.f, gnew = 0.f;
+    // GDN: this step's scalar log-decay (wave-uniform) and the n logged ones,
+    // lane j holding ell_j
+    float gell = 0.f;
+    unsigned glog = (unsigned)tid; // placeholder
     if (OP == GDN) {
-        gprev = (MODE != EAGER && n > 0) ? L[n - 1] : 0.f;
-        gnew = MODE == EAGER ? floor_log_decay(a.ld[sh])
-             : STAGED ? L[n] : FOLDS ? gprev : gprev + floor_log_decay(a.ld[sh]);
+        gell = (MODE == EAGER || FUSED) ? floor_log_decay(a.ld[sh]) : STAGED ? L[n] : 0.f;
+        if (MODE != EAGER && n > 0)
+            glog = __builtin_amdgcn_raw_buffer_load_b32(L_r, lane < n ? (unsigned)lane * 4u : kSkip, 0, 0);
     }
+    // KDA, RWKV6: the n logged per-key log-decays [n][DK], one float4 per
+    // thread ahead of the tile's rows (the first NT*4/DK entries; longer logs
+    // take a second pass)
+    const int nlg4 = KEYLOG ? n * (DK / 4) : 0;
+    auto lg_load = [&](int s) {
+        const int idx = tid + s * NT;
+        return buf_raw4<float>(L_r, idx < nlg4 ? (unsigned)(4 * idx) : kSkipElem);
+    };
+    u32x4 lst = u32x4{(unsigned)tid, 0u, 0u, 0u}; // placeholder, stored to the junk slot
+    if (KEYLOG && wave * 64 < nlg4)
+        lst = lg_load(0);
     // This tile's shard of the n logged value-side factors.
     const rsrc_t b_r = make_rsrc(static_cast<const char *>(a.blog) + (long)sh * M * DV * BS,
                                  MODE == EAGER ? 0 : n * DV * BS);
@@ -526,30 +582,20 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
         const int ci = tid < n ? tid : tid < 2 * n ? M + tid - n : 2 * M;
         cst = __builtin_amdgcn_raw_buffer_load_b32(c_r, tid < 2 * n + 1 ? (unsigned)ci * 4u : kSkip, 0, 0);
     }
-    // log entries for this wave's share of the replay coefficients (FUSED)
-    unsigned ea[EW][KPL], el[EW][KPL]; // raw words
-    float eg[EW];
+    // key-side factors a_m for this wave's share of the replay coefficients (FUSED)
+    unsigned ea[EW][KPL]; // raw words
     const rsrc_t a_r = make_rsrc(static_cast<const TIn *>(a.alog) + (long)sh * M * DK, FUSED ? n * DK * ES : 0);
 #pragma unroll
     for (int e = 0; e < EW; ++e) {
         const int m = wave + NW * e;
-        eg[e] = 0.f;
 #pragma unroll
         for (int c = 0; c < KPL; ++c)
-        {
             ea[e][c] = (unsigned)tid; // placeholders: entries m >= n are never used
-            el[e][c] = (unsigned)tid;
-        }
         if (FUSED && m < n) { // wave-uniform
-            if (OP == GDN)
-                eg[e] = L[m];
 #pragma unroll
             for (int c = 0; c < KPL; ++c) {
                 const int i = lane + 64 * c;
-                const unsigned ei = i < DK ? (unsigned)(m * DK + i) : kSkipElem;
-                ea[e][c] = buf_raw1<TIn>(a_r, ei);
-                if (OP != GDN)
-                    el[e][c] = buf_raw1<float>(L_r, ei);
+                ea[e][c] = buf_raw1<TIn>(a_r, i < DK ? (unsigned)(m * DK + i) : kSkipElem);
             }
         }
     }
@@ -569,60 +615,87 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
         x[p] = buf_ld4_stream(tile_r, xoff, p * RPP * DV * 4);
 
     // ---------------------------------------- 2. publish the small data in LDS --
-    float mq[RW], mk[RW], mprev[RW], mcur[RW], mell[RW], mu[RW];
+    float mq[RW], mk[RW], mell[RW], mu[RW];
 #pragma unroll
     for (int j = 0; j < RW; ++j) {
         mq[j] = cvt1<TIn>(rq_[j], tid + j * NT);
         mk[j] = cvt1<TIn>(rk_[j], tid + j * NT);
-        mprev[j] = n > 0 ? __uint_as_float(rprev[j]) : 0.f; // Lam_{-1} = 0
-        mcur[j] = __uint_as_float(rcur[j]);
-        mell[j] = floor_log_decay(__uint_as_float(rell[j]));
+        // this step's log-decay (a standalone fold adds none)
+        mell[j] = (OP != GDN && !FOLDS) ? floor_log_decay(__uint_as_float(rell[j])) : 0.f;
         mu[j] = __uint_as_float(ru[j]);
     }
-    float lnew_[RW]; // Lam' per row, kept for the key-side append at the end
-#pragma unroll
-    for (int j = 0; j < RW; ++j) {
-        const int i = tid + j * NT;
-        const bool ok = i < DK;
-        // Lam' (the decayed state's cumulative log-decay) and Lam_f (fold)
-        float lnew, lfold;
-        if (OP == GDN) {
-            lnew = lfold = gnew;
-        } else {
-            lnew = MODE == EAGER ? mell[j] : STAGED ? mcur[j] : mprev[j] + mell[j];
-            lfold = FOLDS ? mprev[j] : lnew;
+    // GDN: T = Lam_{n-1} and, in lane m of wave 0, S_m for the coefficient
+    // pass and the fold table (ascending order; all terms are <= 0)
+    float gT = 0.f;
+    if (OP == GDN && MODE != EAGER) {
+        const float gl = __uint_as_float(glog);
+        float gS = 0.f;
+#pragma unroll 1
+        for (int j = 0; j < n; ++j) { // uniform
+            const float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gl), j));
+            gT += v;
+            gS += j > lane ? v : 0.f;
         }
+        if (wave == 0 && lane < n)
+            gsum[lane] = gS;
+    }
+    // GDN: Lam' (a standalone fold: Lam_{n-1}); applied as a scalar after the sums
+    const float gnew = gT + gell;
+    // Per-row tables that depend on T = Lam_{n-1,i}: read weights, fold base
+    // factor and offsets.  T is 0 for an empty log; GDN applies its scalar T
+    // after the sums, so its tables never need it.
+    auto row_tables = [&](int j, float Tr) {
+        const int i = tid + j * NT;
+        const float rd = DELTA ? mell[j] : 0.f; // the delta rule reads the decayed state
         float wq, wk = 0.f;
         if (OP == GDN) {
             wq = mq[j];
             wk = mk[j];
         } else if (OP == KDA) {
-            const float e = expf(lnew);
+            const float e = expf(Tr + rd);
             wq = e * mq[j];
             wk = e * mk[j];
         } else {
-            wq = (MODE == EAGER ? 1.f : expf(mprev[j])) * mq[j];
+            wq = expf(Tr) * mq[j];
         }
-        float *row = dyn + (ok ? i : DK); // this lane's entry of every table (or the pad)
+        float *row = dyn + (i < DK ? i : DK); // this lane's entry of every table (or the pad)
         row[0 * TS] = wq;
         if (DELTA)
             row[1 * TS] = wk;
         if (OP != GDN && MAY_WRITE) {
-            row[2 * TS] = expf(lfold);
-            row[3 * TS] = lfold;
+            row[2 * TS] = expf(Tr + mell[j]); // merges fold to Lam'; a standalone fold to Lam_{n-1}
+            row[3 * TS] = mell[j];
         }
+        if (FUSED)
+            row[7 * TS] = rd;
+    };
+#pragma unroll
+    for (int j = 0; j < RW; ++j) {
+        const int i = tid + j * NT;
+        const bool ok = i < DK;
+        float *row = dyn + (ok ? i : DK);
         if (KAPPA_HERE)
             row[4 * TS] = DELTA ? mq[j] * mk[j] : mq[j] * mu[j] * mk[j];
         if (FUSED) {
             row[5 * TS] = mq[j];
             row[6 * TS] = mk[j];
-            row[7 * TS] = OP == RWKV6 ? mprev[j] : lnew;
             if (merging)
                 (ok ? F + n * DK + i : junk)[0] = mk[j]; // this step's entry folds with k
         }
-        lnew_[j] = lnew;
         if (MODE == EAGER)
             (ok ? F + i : junk)[0] = mk[j]; // the only entry folds with k
+        if (!scan)
+            row_tables(j, 0.f);
+    }
+    if (KEYLOG) { // the logged per-key decays into the per-key table
+        auto lg_store = [&](int s, u32x4 raw) {
+            const int idx = tid + s * NT;
+            *reinterpret_cast<float4 *>(idx < nlg4 ? F + 4 * idx : junk) = cvt4<float>(raw);
+        };
+        lg_store(0, lst);
+#pragma unroll 1
+        for (int s = 1; s * NT < nlg4; ++s) // long logs (behind the tile's rows)
+            lg_store(s, lg_load(s));
     }
     if (MODE != EAGER) {
         auto shard_store = [&](int s, u32x4 raw) {
@@ -642,27 +715,58 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
         (tid < 2 * n + 1 ? cf + tid : junk)[0] = __uint_as_float(cst);
     __syncthreads();
 
+    // ---- 2b. KDA, RWKV6: suffix sums of the logged decays, key by key in
+    //      place (latest entry first, eight entries per LDS round trip); their
+    //      total T = Lam_{n-1} completes the per-row tables
+    if (scan) { // uniform over the workgroup
+#pragma unroll
+        for (int j = 0; j < RW; ++j) {
+            const int i = tid + j * NT;
+            if (i < DK) {
+                float acc = 0.f;
+#pragma unroll 1
+                for (int m0 = n; m0 > 0; m0 -= 8) {
+                    float l[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        l[e] = m0 - 1 - e >= 0 ? F[(m0 - 1 - e) * DK + i] : 0.f;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        if (m0 - 1 - e >= 0) {
+                            F[(m0 - 1 - e) * DK + i] = acc;
+                            acc += l[e];
+                        }
+                    }
+                }
+                row_tables(j, acc);
+            }
+        }
+        __syncthreads();
+    }
+
     // ------------- 3. FUSED: this wave's replay coefficients (and fold rows)
     if (FUSED) {
         // one log entry m from its raw words: c^q_m, c^k_m and (merging) the
         // entry's fold row
-        auto coef_entry = [&](int m, const unsigned *am_raw, const unsigned *lm_raw, float gm) {
-            // GDN: the entry's scalar factor e^{Lam' - Lam_m}
-            const float g = OP == GDN ? expf(gnew - gm) : 1.f;
+        auto coef_entry = [&](int m, const unsigned *am_raw) {
+            // GDN: the entry's scalar factor e^{Lam' - Lam_m} = e^{S_m + ell_t}
+            const float g = OP == GDN ? expf(gsum[m] + gell) : 1.f;
             float sq = 0.f, sk = 0.f;
 #pragma unroll
             for (int c = 0; c < KPL; ++c) {
                 const int i = lane + 64 * c;
                 if (i >= DK)
                     continue;
-                const float am = cvt1<TIn>(am_raw[c], i), lm = __uint_as_float(lm_raw[c]);
-                // e^{Lam_x,i - Lam_m,i} a_m,i (GDN: scalar factor applied after the sum)
-                const float f = OP == GDN ? am : expf(Lx[i] - lm) * am;
+                const float am = cvt1<TIn>(am_raw[c], i);
+                // e^{Lam_x,i - Lam_m,i} a_m,i = e^{S_m,i + read offset} a_m,i
+                // (GDN: scalar factor applied after the sum)
+                const float sm = OP == GDN ? 0.f : F[m * DK + i];
+                const float f = OP == GDN ? am : expf(sm + Lx[i]) * am;
                 sq = fmaf(f, Qr[i], sq);
                 if (DELTA)
                     sk = fmaf(f, Kr[i], sk);
-                if (merging) // fold row: e^{Lam' - Lam_m} a_m
-                    F[m * DK + i] = OP == GDN ? g * am : OP == KDA ? f : expf(Lf[i] - lm) * am;
+                if (merging) // fold row e^{Lam' - Lam_m} a_m, over suffix-sum row m
+                    F[m * DK + i] = OP == GDN ? g * am : OP == KDA ? f : expf(sm + Lf[i]) * am;
             }
             sq = wave_sum_from<1>(sq);
             if (DELTA)
@@ -678,21 +782,19 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
             const int m = wave + NW * e;
             if (m >= n)
                 break; // uniform over the wave
-            coef_entry(m, ea[e], el[e], eg[e]);
+            coef_entry(m, ea[e]);
         }
         // a longer log: one entry per wave at a time, loaded here (behind the
         // tile's rows, so only such long logs wait for them)
 #pragma unroll 1
         for (int m = NW * EW + wave; m < n; m += NW) {
-            unsigned am_raw[KPL], lm_raw[KPL];
+            unsigned am_raw[KPL];
 #pragma unroll
             for (int c = 0; c < KPL; ++c) {
                 const int i = lane + 64 * c;
-                const unsigned ei = i < DK ? (unsigned)(m * DK + i) : kSkipElem;
-                am_raw[c] = buf_raw1<TIn>(a_r, ei);
-                lm_raw[c] = OP != GDN ? buf_raw1<float>(L_r, ei) : 0u;
+                am_raw[c] = buf_raw1<TIn>(a_r, i < DK ? (unsigned)(m * DK + i) : kSkipElem);
             }
-            coef_entry(m, am_raw, lm_raw, OP == GDN ? L[m] : 0.f);
+            coef_entry(m, am_raw);
         }
     }
 
@@ -731,25 +833,28 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
         __syncthreads();
 
     // ------- 5. fold table for MERGE / FOLD (FMERGE, EAGER built theirs above):
-    //    F[m][i] = e^{Lam_f,i - Lam_m,i} a_m,i; in MERGE the entry n appended by
-    //    ReplayPrep (a_n = k, Lam_n = Lam_f) gives exactly k_i.
+    //    F[m][i] = e^{Lam_f,i - Lam_m,i} a_m,i = e^{S_m,i + fold offset} a_m,i,
+    //    written over suffix-sum row m; in MERGE the entry n appended by
+    //    ReplayPrep (a_n = k, at Lam_f itself) gives exactly k_i.
     if (MODE == MERGE || FOLDS) {
         const rsrc_t af_r = make_rsrc(static_cast<const TIn *>(a.alog) + (long)sh * M * DK, nf * DK * ES);
         const int total = nf * DK;
         for (int base = 0; base < total; base += 4 * NT) {
-            float av[4], lv[4];
+            float av[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int idx = base + u * NT + tid;
-                const unsigned ei = idx < total ? (unsigned)idx : kSkipElem;
-                av[u] = buf_ld_in<TIn>(af_r, ei);
-                lv[u] = buf_ld_in<float>(L_r, OP == GDN ? (idx < total ? (unsigned)(idx / DK) : kSkipElem) : ei);
+                av[u] = buf_ld_in<TIn>(af_r, idx < total ? (unsigned)idx : kSkipElem);
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int idx = base + u * NT + tid;
-                if (idx < total)
-                    F[idx] = expf((OP == GDN ? gnew : Lf[idx % DK]) - lv[u]) * av[u];
+                if (idx < total) {
+                    const int m = idx / DK;
+                    const float ex = m >= n ? 1.f
+                                   : expf(OP == GDN ? gsum[m] + gell : F[idx] + Lf[idx % DK]);
+                    F[idx] = ex * av[u];
+                }
             }
         }
     }
@@ -832,7 +937,8 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
         }
     }
 
-    // Key-side append of entry n (a_n = k, Lam_n = Lam'), by tile 0, issued
+    // Key-side append of entry n (a_n = k and this step's floored log-decay
+    // ell_n, whose running sum is the pages' snapshot Lam_n), by tile 0, issued
     // last: stores count against the same wait counter as loads, so a store
     // issued earlier would hold up the wait for the tile's rows.
     if (FUSED && !merging && tile == 0) {
@@ -845,11 +951,11 @@ __global__ __launch_bounds__((TileCfg<DK, DV>::NT)) void step_kernel(StepArgs a)
                 if (sizeof(TIn) == 4 || (i & 1) == 0)
                     *reinterpret_cast<unsigned *>(static_cast<TIn *>(a.alog) + ((long)sh * M + n) * DK + i) = rk_[j];
                 if (OP != GDN)
-                    L[(long)n * DK + i] = lnew_[j];
+                    L[(long)n * DK + i] = mell[j];
             }
         }
         if (OP == GDN && tid == 0)
-            L[n] = gnew;
+            L[n] = gell;
     }
 
     // --------------------------------------- 7. fold and write the tile once
@@ -923,7 +1029,7 @@ hipError_t launch_step_t(const StepArgs &a, hipStream_t st)
     const int slot_heads = (MODE == SFOLD && a.slot >= 0) ? a.H : a.BH;
     const int n_lds = (MODE == SSTEP || MODE == SFOLD) ? a.M - 1 : a.n;
     const dim3 grid((unsigned)slot_heads * C::NTILE);
-    const size_t lds = sizeof(float) * (size_t)dyn_floats(MODE, n_lds, DK, C::T);
+    const size_t lds = sizeof(float) * (size_t)dyn_floats(OP, MODE, n_lds, DK, C::T);
     hipLaunchKernelGGL((step_kernel<OP, TIn, DK, DV, MODE>), grid, dim3(C::NT), lds, st, a);
     return hipGetLastError();
 }

@@ -978,3 +978,76 @@ def test_full_decay_long_log(orc, op, path):
     run.merge()
     _report(run, f"full decay, long log, {op} {path}")
     run.close()
+
+
+def _wipe_schedule(w):
+    """Deterministic repeated full forgetting in an M=32 log, one pattern per
+    slot-head (steps t of each 32-step cycle wiped with a log-decay of -inf:
+    key 0 for KDA/RWKV6, the whole head for GDN):
+      slot-head 0: t = 0..30 (every append step of the cycle; the merge step
+                   decays normally),
+      slot-heads 1, 2, 3: t < 24, 16, 8, then ordinary decays (cumulative
+                   snapshots would lose the later decays' low bits here),
+      slot-head 4: every other step,
+      slot-head 5: no wipe.
+    q and k put most of their weight on key 0, so the output follows that
+    key's decay factors."""
+    pats = [lambda t: t < 31, lambda t: t < 24, lambda t: t < 16, lambda t: t < 8,
+            lambda t: t % 2 == 0, lambda t: False]
+    steps = []
+    for t in range(w.steps):
+        s = {k_: (None if v_ is None else v_.copy()) for k_, v_ in synth.step(w, t).items()}
+        BH = w.BH
+        for name in ("q", "k"):
+            x = s[name].reshape(BH, w.dk)
+            x[:, 0] = 4.0 * np.sign(x[:, 0] + 1e-3)
+            if w.op != "rwkv6":
+                x /= np.linalg.norm(x, axis=1, keepdims=True)
+            s[name] = synth.round_bf16(x.reshape(w.B, w.H, w.dk))
+        ld = s["ld"].reshape(BH, -1)
+        for sh in range(BH):
+            if pats[sh % len(pats)](t % w.M):
+                ld[sh, 0 if w.op != "gdn" else slice(None)] = -np.inf
+        s["ld"] = ld.reshape(s["ld"].shape)
+        steps.append(s)
+    return steps
+
+
+@needs_gpu
+@pytest.mark.parametrize("op", ["gdn", "kda", "rwkv6"])
+@pytest.mark.parametrize("path", ["fused", "staged", "per-slot"])
+def test_repeated_full_forgetting_worst_case(orc, op, path):
+    """Up to 31 full-forgetting steps of one key (one head for GDN) inside one
+    M=32 log, followed by ordinary decays, two cycles: every output and both
+    merged states match the oracle at the fp32 bar, per slot-head (the
+    factors are sums of the logged decays, so the wipes cost no precision)."""
+    import recurrent_state_update_amd as rsu
+    w = synth.Workload(77, op, 2, 3, 64, 64, 32, 64, "bf16")
+    steps = _wipe_schedule(w)
+    X0, u = synth.initial(w)
+    dt = torch.bfloat16
+    base = dev(X0)
+    st = rsu.DeltaLogState(op, w.B, w.H, w.dk, w.dv, w.M, dtype=dt, base=base, u=dev(u))
+    if path == "per-slot":
+        st.enable_slots()
+    X = X0.reshape(1, w.BH, w.dk, w.dv).astype(np.float64).copy()
+    u_sub = None if u is None else u[np.arange(w.BH) % w.H].astype(np.float64)
+    worst_o = worst_S = 0.0
+    merges = 0
+    for t, s in enumerate(steps):
+        d_ = {k_: dev(v_, dt if k_ in ("q", "k", "v") else torch.float32) for k_, v_ in s.items()}
+        if path == "staged":
+            st.replay_prep(d_["q"], d_["k"], d_["ld"])
+            o = st.append_decode(d_["q"], d_["k"], d_["v"], d_["beta"])
+        else:
+            o = st.step(d_["q"], d_["k"], d_["v"], d_["beta"], d_["ld"])
+        sub = synth.subset(s, np.arange(w.BH))
+        o_ref = orc.eager_step(op, X, sub["q"], sub["k"], sub["v"], sub["beta"], sub["ld"], u_sub)[0]
+        worst_o = max(worst_o, rel(o.reshape(w.BH, w.dv).cpu().numpy(), o_ref))
+        if (t + 1) % w.M == 0:
+            merges += 1
+            worst_S = max(worst_S, rel(base.reshape(w.BH, w.dk, w.dv).cpu().numpy(), X[0]))
+    print(f"[{op} {path} wipes M=32] worst o={worst_o:.2e} S={worst_S:.2e}", flush=True)
+    st.close()
+    assert merges == 2
+    assert worst_o < FP32_TOL and worst_S < FP32_TOL
