@@ -81,7 +81,8 @@ typedef enum {
     DL_E_SHAPE = 2,   /* d_k or d_v not supported, or the state too large */
     DL_E_ALIGN = 3,   /* a pointer is not aligned as required above */
     DL_E_HIP = 4,     /* a HIP launch failed */
-    DL_E_STATE = 5    /* call out of order (e.g. append without replay prep) */
+    DL_E_STATE = 5,   /* call out of order (e.g. append without replay prep) */
+    DL_E_SCRATCH = 6  /* dl_decode_step_staged_noalloc: shape beyond its static scratch */
 } dl_status;
 
 typedef struct dl_state dl_state; /* opaque host-side handle */
@@ -133,6 +134,24 @@ dl_status dl_replay_prep(dl_state *s, const void *q, const void *k, const float 
  * (one dense write).  DL_E_STATE unless dl_replay_prep ran just before. */
 dl_status dl_append_decode(dl_state *s, const void *q, const void *k, const void *v,
                            const float *beta, float *o, void *stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * two-stage step (dl_replay_prep then dl_append_decode) in one call whose
+ * per-step replay coefficients live in a static device buffer of the library
+ * instead of the workspace.  It allocates nothing; inputs, outputs and the
+ * handle's base and workspace are as for dl_decode_step, and it leaves the
+ * handle exactly as that pair of calls would (results agree bit for bit).
+ * Limit: B*H*(2M+2) <= 2^20 floats (4 MiB; e.g. B*H = 8192 at M = 32),
+ * otherwise DL_E_SCRATCH before any HIP call.  Each GPU has one such buffer,
+ * shared by every call on it: calls that overlap in time on one GPU (on
+ * different streams or host threads) race and must not be issued; calls
+ * ordered on one stream are safe.  The calling thread's current device must
+ * be the one that holds the handle's buffers and the stream.  The first call
+ * on a device looks up the buffer's address (DL_E_HIP if that fails). */
+dl_status dl_decode_step_staged_noalloc(dl_state *s, const void *q, const void *k, const void *v,
+                                        const float *beta, const float *log_decay, float *o,
+                                        void *stream);
 
 /* Merge now ("Core mechanism: Base + Log", the merge phase, taken before its
  * M-th step): fold the n pending entries into S-bar with one dense write so

@@ -26,12 +26,12 @@ LIB_PATH = os.path.join(_HERE, "libdeltalog.so")
 OPS = {"gdn": 0, "kda": 1, "rwkv6": 2}
 DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 STATUS = {0: "DL_OK", 1: "DL_E_INVALID", 2: "DL_E_SHAPE", 3: "DL_E_ALIGN", 4: "DL_E_HIP",
-          5: "DL_E_STATE"}
+          5: "DL_E_STATE", 6: "DL_E_SCRATCH"}
 EXPORTS = ("dl_workspace_bytes", "dl_state_create", "dl_decode_step", "dl_replay_prep",
            "dl_append_decode", "dl_merge", "dl_state_reset", "dl_log_len", "dl_set_log_len",
            "dl_state_destroy", "dl_eager_step", "dl_status_string", "dl_suggest_merge_interval",
            "dl_state_enable_slots", "dl_slot_admit", "dl_slot_merge", "dl_slot_log_len",
-           "dl_slot_release")
+           "dl_slot_release", "dl_decode_step_staged_noalloc")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run `python recurrent_state_update_amd/_build.py` "
@@ -58,6 +58,7 @@ _SIG = {
     "dl_slot_merge": ([_p, _i, _p], _i),
     "dl_slot_log_len": ([_p, _i], _i),
     "dl_slot_release": ([_p, _i, _p], _i),
+    "dl_decode_step_staged_noalloc": ([_p] * 8, _i),
 }
 for _name, (_args, _res) in _SIG.items():
     _f = getattr(_lib, _name)
@@ -113,6 +114,11 @@ def dl_state_create(B, H, d_k, d_v, M, op, in_dtype, base, workspace, u):
 def dl_decode_step(s, q, k, v, beta, log_decay, o, stream=None):
     return _lib.dl_decode_step(s, _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_decay),
                                _ptr(o), _stream(stream))
+
+
+def dl_decode_step_staged_noalloc(s, q, k, v, beta, log_decay, o, stream=None):
+    return _lib.dl_decode_step_staged_noalloc(s, _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                                              _ptr(log_decay), _ptr(o), _stream(stream))
 
 
 def dl_replay_prep(s, q, k, log_decay, stream=None):

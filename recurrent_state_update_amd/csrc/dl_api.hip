@@ -12,10 +12,21 @@
 // ReplayPrep work done inside each AppendDecode workgroup); dl_replay_prep +
 // dl_append_decode run it as the two-stage split, ReplayPrep once per
 // slot-head then AppendDecode per value tile.  Both compute the same step.
+#include <mutex>
 #include <new>
 
 #include "deltalog.h"
 #include "dl_internal.h"
+
+// Scratch of dl_decode_step_staged_noalloc: the per-step replay coefficient
+// rows ([B*H][2M+2] floats) that ReplayPrep writes and AppendDecode reads,
+// held in module memory so that the call allocates nothing.  Every GPU the
+// library runs on has its own copy, kept until the process ends; each call
+// on a GPU reuses that GPU's copy, so calls that overlap on one GPU race.
+// Every coefficient the second stage reads is written by the first stage of
+// the same call, so nothing here needs clearing between calls.
+static constexpr size_t kScratchFloats = size_t(1) << 20; // 4 MiB
+static __device__ __align__(256) float scratch[kScratchFloats];
 
 struct dl_state {
     int B, H, dk, dv, M;
@@ -184,6 +195,29 @@ dl::StepArgs make_args(const dl_state *s)
 }
 
 int *slot_phases(const dl_state *s) { return reinterpret_cast<int *>(s->ws + s->lay.t_off); }
+
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current.  In host code the array's name is only a
+// host-side stand-in: kernels must be given this address.
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+float *scratch_addr[kMaxDevices];
+
+dl_status scratch_on_current_device(float **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return DL_E_HIP;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_addr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return DL_E_HIP;
+        scratch_addr[dev] = static_cast<float *>(p);
+    }
+    *out = scratch_addr[dev];
+    return DL_OK;
+}
 
 hipError_t launch_prep(int op, int dtype, int dk, const dl::StepArgs &a, hipStream_t st)
 {
@@ -362,6 +396,41 @@ dl_status dl_decode_step(dl_state *s, const void *q, const void *k, const void *
     if (launch_step(s->op, s->dtype, s->dk, s->dv, merge ? dl::FMERGE : dl::FAPPEND, a,
                     static_cast<hipStream_t>(stream)) !=
         hipSuccess)
+        return DL_E_HIP;
+    s->n = merge ? 0 : s->n + 1;
+    return DL_OK;
+}
+
+dl_status dl_decode_step_staged_noalloc(dl_state *s, const void *q, const void *k, const void *v,
+                                        const float *beta, const float *log_decay, float *o,
+                                        void *stream)
+{
+    if (!s)
+        return DL_E_INVALID;
+    if (s->prepped || s->per_slot)
+        return DL_E_STATE;
+    dl_status st = check_step_ptrs(s->op, s->dtype, q, k, v, beta, log_decay, o, true);
+    if (st == DL_OK)
+        st = check_handle_step_overlaps(s, q, k, v, beta, log_decay, o);
+    if (st != DL_OK)
+        return st;
+    if ((size_t)s->B * s->H * s->lay.cstride > kScratchFloats)
+        return DL_E_SCRATCH;
+    float *coef = nullptr;
+    if ((st = scratch_on_current_device(&coef)) != DL_OK)
+        return st;
+    dl::StepArgs a = make_args(s);
+    a.coef = coef; // the coefficient rows live in the static scratch, not the workspace
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.beta = beta;
+    a.ld = log_decay;
+    a.o = o;
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    const bool merge = s->n + 1 == s->M;
+    if (launch_prep(s->op, s->dtype, s->dk, a, hs) != hipSuccess ||
+        launch_step(s->op, s->dtype, s->dk, s->dv, merge ? dl::MERGE : dl::APPEND, a, hs) != hipSuccess)
         return DL_E_HIP;
     s->n = merge ? 0 : s->n + 1;
     return DL_OK;
@@ -571,6 +640,7 @@ const char *dl_status_string(dl_status st)
     case DL_E_ALIGN: return "misaligned pointer";
     case DL_E_HIP: return "HIP launch failed";
     case DL_E_STATE: return "call out of order";
+    case DL_E_SCRATCH: return "shape needs more scratch than the library's static buffer holds";
     }
     return "unknown status";
 }

@@ -16,7 +16,7 @@ from recurrent_state_update_amd import _lib
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "deltalog.h")
 
-OK, INVALID, SHAPE, ALIGN, HIP, STATE = range(6)
+OK, INVALID, SHAPE, ALIGN, HIP, STATE, SCRATCH = range(7)
 GDN, KDA, RWKV6 = 0, 1, 2
 F32, BF16 = 0, 1
 # fake device addresses: aligned, never dereferenced by these tests
@@ -43,7 +43,7 @@ def test_every_declared_function_is_exported():
 
 
 def test_status_strings():
-    for st in range(6):
+    for st in range(7):
         assert rsu.dl_status_string(st)
     assert rsu.dl_status_string(99) == "unknown status"
 
@@ -234,3 +234,32 @@ def test_overlapping_buffers_are_rejected():
     assert e(GDN, 2, 3, 16, 16, F32, BASE, BASE, K, V, BETA, LD, None, O, s) == INVALID       # q in S
     assert e(RWKV6, 2, 3, 16, 16, F32, BASE, Q, K, V, None, LD, BASE + 16, O, s) == INVALID   # u in S
     assert e(GDN, 2, 3, 16, 16, F32, BASE, Q, K, V, BETA, LD, None, K + 256, s) == INVALID   # o over k
+
+
+def test_noalloc_staged_step_validation():
+    """dl_decode_step_staged_noalloc rejects bad calls before any HIP call:
+    null or misaligned pointers, a missing log-decay, an output overlapping
+    the base, and a shape whose coefficient rows exceed the static scratch
+    (B*H*(2M+2) > 2^20 floats: DL_E_SCRATCH).  (The out-of-order cases need
+    a launch first and are checked on the GPU.)"""
+    f = lambda *a: rsu.dl_decode_step_staged_noalloc(*a, 0)  # stream 0: no torch stream needed
+    st, h = _create(B=2, H=3, dk=16, dv=16, M=4)
+    assert st == OK
+    assert f(None, Q, K, V, BETA, LD, O) == INVALID
+    assert f(h, None, K, V, BETA, LD, O) == INVALID
+    assert f(h, Q, K, V, None, LD, O) == INVALID        # beta needed by GDN
+    assert f(h, Q, K, V, BETA, None, O) == INVALID      # the log-decay is read
+    assert f(h, Q, K, V, BETA, LD, O + 4) == ALIGN
+    assert f(h, Q, K, V, BETA, LD, BASE) == INVALID     # o overlaps the base
+    assert rsu.dl_log_len(h) == 0
+    rsu.dl_state_destroy(h)
+    # 8192 slot-heads at M = 32: 8192 * 66 floats fit; 16384 do not
+    far_base, far_ws = 0x7e0000000000, 0x7d0000000000  # far apart: large shapes
+    st, h = _create(B=64, H=128, dk=16, dv=16, M=32, base=far_base, ws=far_ws)
+    assert st == OK
+    rsu.dl_state_destroy(h)
+    st, h = _create(B=128, H=128, dk=16, dv=16, M=32, base=far_base, ws=far_ws)
+    assert st == OK
+    assert f(h, Q, K, V, BETA, LD, O) == SCRATCH
+    assert rsu.dl_log_len(h) == 0                        # nothing ran
+    rsu.dl_state_destroy(h)
