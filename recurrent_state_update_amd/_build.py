@@ -21,7 +21,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdeltalog.so")
-SOURCES = ["dl_api.hip", "dl_gdn.hip", "dl_kda.hip", "dl_rwkv6.hip"]
+SOURCES = ["dl_api.hip", "dl_device.hip", "dl_gdn.hip", "dl_kda.hip", "dl_rwkv6.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

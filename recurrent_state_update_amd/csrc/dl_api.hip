@@ -12,21 +12,15 @@
 // ReplayPrep work done inside each AppendDecode workgroup); dl_replay_prep +
 // dl_append_decode run it as the two-stage split, ReplayPrep once per
 // slot-head then AppendDecode per value tile.  Both compute the same step.
-#include <mutex>
+//
+// This file is plain host code: kernels are reached only through the
+// launchers declared in dl_internal.h (dl_gdn.hip, dl_kda.hip, dl_rwkv6.hip,
+// dl_device.hip), so it also builds with a host compiler alone, as the
+// sanitizer test does.
 #include <new>
 
 #include "deltalog.h"
 #include "dl_internal.h"
-
-// Scratch of dl_decode_step_staged_noalloc: the per-step replay coefficient
-// rows ([B*H][2M+2] floats) that ReplayPrep writes and AppendDecode reads,
-// held in module memory so that the call allocates nothing.  Every GPU the
-// library runs on has its own copy, kept until the process ends; each call
-// on a GPU reuses that GPU's copy, so calls that overlap on one GPU race.
-// Every coefficient the second stage reads is written by the first stage of
-// the same call, so nothing here needs clearing between calls.
-static constexpr size_t kScratchFloats = size_t(1) << 20; // 4 MiB
-static __device__ __align__(256) float scratch[kScratchFloats];
 
 struct dl_state {
     int B, H, dk, dv, M;
@@ -65,25 +59,6 @@ Layout workspace_layout(long B, long H, int dk, int dv, int M, int op, int dtype
     l.t_off = round_up(l.c_off + (size_t)BH * l.cstride * 4, 256);
     l.total = round_up(l.t_off + (size_t)B * 4, 256);
     return l;
-}
-
-// Set the phase of one slot (or of all when slot < 0, skipping released
-// slots when active_only).  A kernel rather than a memset so that calls stay
-// capturable into HIP graphs.
-__global__ void slot_phase_kernel(int *t0, int B, int slot, int value, int active_only)
-{
-    const int b = blockIdx.x * blockDim.x + threadIdx.x;
-    if (b < B && (slot < 0 || b == slot) && !(active_only && t0[b] < 0))
-        t0[b] = value;
-}
-
-hipError_t launch_slot_phase(int *t0, int B, int slot, int value, bool active_only, hipStream_t st)
-{
-    const int blocks = slot >= 0 ? 1 : (B + 255) / 256;
-    const int first = slot >= 0 ? slot : 0;
-    hipLaunchKernelGGL(slot_phase_kernel, dim3(blocks), dim3(slot >= 0 ? 1 : 256), 0, st,
-                       t0 + first, slot >= 0 ? 1 : B, slot >= 0 ? 0 : -1, value, active_only ? 1 : 0);
-    return hipGetLastError();
 }
 
 } // namespace dl
@@ -195,29 +170,6 @@ dl::StepArgs make_args(const dl_state *s)
 }
 
 int *slot_phases(const dl_state *s) { return reinterpret_cast<int *>(s->ws + s->lay.t_off); }
-
-// Device address of `scratch` on the current device, looked up once per
-// device with that device current.  In host code the array's name is only a
-// host-side stand-in: kernels must be given this address.
-constexpr int kMaxDevices = 64;
-std::mutex scratch_mu;
-float *scratch_addr[kMaxDevices];
-
-dl_status scratch_on_current_device(float **out)
-{
-    int dev = -1;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
-        return DL_E_HIP;
-    std::lock_guard<std::mutex> lock(scratch_mu);
-    if (!scratch_addr[dev]) {
-        void *p = nullptr;
-        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
-            return DL_E_HIP;
-        scratch_addr[dev] = static_cast<float *>(p);
-    }
-    *out = scratch_addr[dev];
-    return DL_OK;
-}
 
 hipError_t launch_prep(int op, int dtype, int dk, const dl::StepArgs &a, hipStream_t st)
 {
@@ -414,11 +366,11 @@ dl_status dl_decode_step_staged_noalloc(dl_state *s, const void *q, const void *
         st = check_handle_step_overlaps(s, q, k, v, beta, log_decay, o);
     if (st != DL_OK)
         return st;
-    if ((size_t)s->B * s->H * s->lay.cstride > kScratchFloats)
+    if ((size_t)s->B * s->H * s->lay.cstride > dl::kScratchFloats)
         return DL_E_SCRATCH;
     float *coef = nullptr;
-    if ((st = scratch_on_current_device(&coef)) != DL_OK)
-        return st;
+    if (dl::scratch_on_current_device(&coef) != hipSuccess)
+        return DL_E_HIP;
     dl::StepArgs a = make_args(s);
     a.coef = coef; // the coefficient rows live in the static scratch, not the workspace
     a.q = q;

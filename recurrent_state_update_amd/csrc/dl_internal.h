@@ -2,7 +2,7 @@
 // libdeltalog.  Not installed; the public interface is include/deltalog.h.
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -71,6 +71,11 @@ hipError_t launch_prep_rwkv6(int dtype, int dk, const StepArgs &a, hipStream_t s
 // Set slot phases: one slot (slot >= 0), or all slots (slot < 0; with
 // active_only, only those not released).  A kernel, so calls stay capturable.
 hipError_t launch_slot_phase(int *t0, int B, int slot, int value, bool active_only, hipStream_t st);
+// The static device scratch of dl_decode_step_staged_noalloc (dl_device.hip):
+// its size in floats, and its device address on the current device (looked
+// up once per device).
+constexpr size_t kScratchFloats = size_t(1) << 20; // 4 MiB
+hipError_t scratch_on_current_device(float **out);
 hipError_t launch_step_gdn(int dtype, int dk, int dv, int mode, const StepArgs &a, hipStream_t st);
 hipError_t launch_step_kda(int dtype, int dk, int dv, int mode, const StepArgs &a, hipStream_t st);
 hipError_t launch_step_rwkv6(int dtype, int dk, int dv, int mode, const StepArgs &a, hipStream_t st);

@@ -46,6 +46,8 @@
 // waves share a SIMD.
 #pragma once
 
+#include <hip/hip_runtime.h>
+
 #include "dl_internal.h"
 
 #ifndef DL_TILE_MAX
