@@ -582,6 +582,105 @@ def pages_context(res):
     }
 
 
+# ------------------------------------------- merge interval from measurement --
+CHOOSE_SWEEP = tuple(range(1, 21)) + (24, 28, 32)
+
+
+def _fixed_n_launch_us(st, launch, n, pool, G=16, reps=8):
+    """Mean us of one launch on handle st with its log held at n entries
+    (dl_set_log_len before each launch): G such launches captured in a HIP
+    graph, replayed twice untimed, then `reps` times between HIP events."""
+    import torch
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sp = torch.cuda.current_stream().cuda_stream
+        for i in range(G):
+            st.set_log_len(n)
+            launch(0, i % pool, sp)
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) * 1e3 / (reps * G)
+
+
+def choose_merge_interval(w, pool: int, repeats: int = 3, max_M: int = 32) -> dict:
+    """The merge interval from measured launch times, next to a measured sweep
+    of M on the same shape (one state, as the large-batch sweep runs it).
+
+    Calibration: for every log length n < max_M, the time of an append launch
+    with the log held at n entries (a handle with M = max_M after max_M - 1
+    real steps, dl_set_log_len(n) before each launch) and of a merge launch at
+    n (a handle with M = n + 1 after n real steps), each over graph replays.
+    dl_choose_merge_interval takes these two tables.  Sweep: whole merge
+    cycles at every M in CHOOSE_SWEEP and at each suggested M, the median of
+    `repeats` passes in alternating order.  Reports the M each model (time,
+    and the byte model of dl_suggest_merge_interval) suggests and how far its
+    measured time per decode step lies above the measured best."""
+    import torch
+    import synth
+    import recurrent_state_update_amd as rsu
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    inp = stage_inputs(w, pool, dt)
+    X0, u = synth.initial(w)
+    base = torch.from_numpy(X0).cuda()
+    u_dev = None if u is None else torch.from_numpy(u).cuda()
+    o = torch.empty(w.B, w.H, w.dv, device="cuda")
+
+    def handle(M):
+        return rsu.DeltaLogState(w.op, w.B, w.H, w.dk, w.dv, M, dtype=dt, base=base, u=u_dev)
+
+    sp = lambda: torch.cuda.current_stream().cuda_stream
+    st = handle(max_M)
+    la = deltalog_launcher(w, inp, [st], o)
+    for i in range(max_M - 1):           # a full log of real entries
+        la(0, i % pool, sp())
+    app = [_fixed_n_launch_us(st, la, n, pool) for n in range(max_M - 1)]
+    st.close()
+    mer = []
+    for n in range(max_M):
+        st = handle(n + 1)
+        lm = deltalog_launcher(w, inp, [st], o)
+        for i in range(n):               # n real entries, then merges at n
+            lm(0, i % pool, sp())
+        mer.append(_fixed_n_launch_us(st, lm, n, pool))
+        st.close()
+    timed_M = rsu.dl_choose_merge_interval(app, mer, max_M)
+    bytes_M = rsu.dl_suggest_merge_interval(w.B, w.H, w.dk, w.dv, rsu.OPS[w.op], rsu.DTYPES[dt])
+    log(f"{w.describe()}: suggested M = {timed_M} (from calibrated launch times), {bytes_M} (from bytes)")
+
+    Ms = sorted(set(CHOOSE_SWEEP) | {timed_M, bytes_M})
+    runs = {M: [] for M in Ms}
+    for rep in range(repeats):
+        for M in (Ms if rep % 2 == 0 else reversed(Ms)):
+            base.copy_(torch.from_numpy(X0))
+            st = handle(M)
+            K = max(4, -(-256 // M))
+            ms = time_cycles(deltalog_launcher(w, inp, [st], o), 1, M, pool, K, 2, graphs=True)
+            runs[M].append(ms * 1e3)
+            st.close()
+    sweep = {M: float(np.median(v)) for M, v in runs.items()}
+    best = min(sweep, key=sweep.get)
+    del inp
+    torch.cuda.empty_cache()
+    return dict(workload=w.describe(), rotate_states=1,
+                calibration_us=dict(append=[round(x, 3) for x in app], merge=[round(x, 3) for x in mer]),
+                suggested_M_from_time=timed_M, suggested_M_from_bytes=bytes_M,
+                sweep_us_per_decode_step={str(M): round(v, 3) for M, v in sweep.items()},
+                sweep_value={str(M): round(w.BH / (v * 1e-6), 1) for M, v in sweep.items()},
+                measured_best_M=best,
+                gap_time_model=round(sweep[timed_M] / sweep[best] - 1.0, 5),
+                gap_byte_model=round(sweep[bytes_M] / sweep[best] - 1.0, 5))
+
+
 # -------------------------------------------------------------------- main --
 def main():
     ap = argparse.ArgumentParser()
@@ -599,6 +698,9 @@ def main():
     ap.add_argument("--no-others", action="store_true", help="skip the KDA / RWKV6 workloads")
     ap.add_argument("--quick", action="store_true",
                     help="the headline and the eager baseline only (for counter runs)")
+    ap.add_argument("--choose-M", action="store_true",
+                    help="workload 4 only: calibrate launch costs, suggest M from them and from "
+                         "bytes, and sweep M to find the measured best (one JSON line)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB, 10 times (the "
                          "reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -648,6 +750,9 @@ def main():
         w = w.with_(H=args.H)
     K, W, R = args.steps, args.warmup, args.rotate
     pool = args.pool or min(w.steps, 256 if w.B <= 128 else 64)
+    if args.choose_M:
+        print(json.dumps({"choose_M": choose_merge_interval(w, pool)}), flush=True)
+        return
     res = bench_workload(w, K, W, R, pool, quick=args.quick)
     default_shape = args.workload == 1 and not args.M and not args.B and not args.H
     res["roofline"]["traffic"] = measured_traffic() if default_shape else None

@@ -203,6 +203,21 @@ dl_status dl_eager_step(dl_op op, int B, int H, int d_k, int d_v, dl_dtype in_dt
  * Returns 0 for invalid arguments. */
 int dl_suggest_merge_interval(int B, int H, int d_k, int d_v, dl_op op, dl_dtype in_dtype);
 
+/* The merge interval M in [1, max_M] that minimises the mean time per decode
+ * step over a merge cycle, predicted from measured launch times (the
+ * "Traffic model" trade-off of the gist.science summary, priced in measured
+ * time instead of modelled bytes: M-1 appends whose log replay grows with
+ * the log, then one merge whose dense write the M steps share):
+ *   time(M) = ( append_us[0] + ... + append_us[M-2] + merge_us[M-1] ) / M.
+ * append_us[n] is the time of one dl_decode_step launch that appends with n
+ * entries in the log, merge_us[n] that of one that merges with n entries in
+ * the log (folding n + 1), both for the caller's shape; each array holds
+ * max_M host doubles (append_us[max_M-1] is not read).  A calibration takes
+ * them by timing launches with the log held at each length (dl_set_log_len),
+ * as `bench.py --choose-M` does.  The smallest such M on ties.  Returns 0 for
+ * a NULL array, a negative or non-finite time, or max_M outside [1, 32]. */
+int dl_choose_merge_interval(const double *append_us, const double *merge_us, int max_M);
+
 /* ------------------------------------------------------------------------
  * Per-slot logs, for continuous batching.  The pages apply the schedule per
  * (slot, head) ("Kernel implementation": ReplayPrep runs per slot-head); with

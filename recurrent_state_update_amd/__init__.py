@@ -31,7 +31,7 @@ EXPORTS = ("dl_workspace_bytes", "dl_state_create", "dl_decode_step", "dl_replay
            "dl_append_decode", "dl_merge", "dl_state_reset", "dl_log_len", "dl_set_log_len",
            "dl_state_destroy", "dl_eager_step", "dl_status_string", "dl_suggest_merge_interval",
            "dl_state_enable_slots", "dl_slot_admit", "dl_slot_merge", "dl_slot_log_len",
-           "dl_slot_release", "dl_decode_step_staged_noalloc")
+           "dl_slot_release", "dl_decode_step_staged_noalloc", "dl_choose_merge_interval")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run `python recurrent_state_update_amd/_build.py` "
@@ -39,6 +39,8 @@ if not os.path.exists(LIB_PATH):
 
 _lib = ctypes.CDLL(LIB_PATH)
 _i, _p, _sz = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+
+
 _SIG = {
     "dl_workspace_bytes": ([_i] * 7, _sz),
     "dl_state_create": ([_i] * 7 + [_p, _p, _p, ctypes.POINTER(_p)], _i),
@@ -59,6 +61,7 @@ _SIG = {
     "dl_slot_log_len": ([_p, _i], _i),
     "dl_slot_release": ([_p, _i, _p], _i),
     "dl_decode_step_staged_noalloc": ([_p] * 8, _i),
+    "dl_choose_merge_interval": ([ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double), _i], _i),
 }
 for _name, (_args, _res) in _SIG.items():
     _f = getattr(_lib, _name)
@@ -157,6 +160,17 @@ def dl_eager_step(op, B, H, d_k, d_v, in_dtype, S, q, k, v, beta, log_decay, u, 
 
 def dl_suggest_merge_interval(B, H, d_k, d_v, op, in_dtype) -> int:
     return int(_lib.dl_suggest_merge_interval(B, H, d_k, d_v, op, in_dtype))
+
+
+def dl_choose_merge_interval(append_us, merge_us, max_M=None) -> int:
+    """append_us[n], merge_us[n]: measured launch times (us) at log length n;
+    max_M defaults to their length."""
+    max_M = len(merge_us) if max_M is None else max_M
+    A = (ctypes.c_double * max(len(append_us), 1))(*append_us)
+    Mg = (ctypes.c_double * max(len(merge_us), 1))(*merge_us)
+    if len(append_us) < max_M - 1 or len(merge_us) < max_M:
+        raise ValueError("want max_M - 1 append times and max_M merge times")
+    return int(_lib.dl_choose_merge_interval(A, Mg, max_M))
 
 
 def dl_state_enable_slots(s, stream=None):

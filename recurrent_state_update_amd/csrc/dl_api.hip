@@ -583,6 +583,29 @@ int dl_suggest_merge_interval(int B, int H, int d_k, int d_v, dl_op op, dl_dtype
     return best;
 }
 
+int dl_choose_merge_interval(const double *append_us, const double *merge_us, int max_M)
+{
+    if (!append_us || !merge_us || max_M < 1 || max_M > 32)
+        return 0;
+    for (int n = 0; n < max_M; ++n) {
+        const double a = n + 1 < max_M ? append_us[n] : 0.0, m = merge_us[n];
+        if (!(a >= 0.0) || !(m >= 0.0) || a > 1e30 || m > 1e30) // NaN fails >= 0
+            return 0;
+    }
+    int best = 1;
+    double best_t = 0.0, appends = 0.0; // appends = sum of append_us[0..M-2]
+    for (int M = 1; M <= max_M; ++M) {
+        if (M >= 2)
+            appends += append_us[M - 2];
+        const double t = (appends + merge_us[M - 1]) / M;
+        if (M == 1 || t < best_t) {
+            best = M;
+            best_t = t;
+        }
+    }
+    return best;
+}
+
 const char *dl_status_string(dl_status st)
 {
     switch (st) {

@@ -8,6 +8,7 @@
 // Exit status 0 when every check holds.
 #include "dl_api.hip"
 
+#include <cmath>
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
@@ -261,6 +262,21 @@ static void test_eager_and_suggest()
         CHECK(m >= 1 && m <= 32);
     }
     CHECK(dl_suggest_merge_interval(64, 32, 24, 128, DL_OP_GDN, DL_BF16) == 0);
+    double app[32], mer[32];
+    for (int n = 0; n < 32; ++n) {
+        app[n] = 25.0 + 0.3 * n;
+        mer[n] = 48.0 + 0.3 * n;
+    }
+    const int m = dl_choose_merge_interval(app, mer, 32);
+    CHECK(m > 1 && m < 32);
+    CHECK(dl_choose_merge_interval(app, mer, 1) == 1);
+    CHECK(dl_choose_merge_interval(nullptr, mer, 32) == 0 && dl_choose_merge_interval(app, nullptr, 32) == 0);
+    CHECK(dl_choose_merge_interval(app, mer, 0) == 0 && dl_choose_merge_interval(app, mer, 33) == 0);
+    app[3] = -1.0;
+    CHECK(dl_choose_merge_interval(app, mer, 32) == 0);
+    app[3] = 25.9;
+    mer[5] = std::nan("");
+    CHECK(dl_choose_merge_interval(app, mer, 32) == 0);
 }
 
 int main()

@@ -146,28 +146,35 @@ def test_binding_names_bad_operator_and_dtype():
         rsu.eager_step("gdn", S, torch.zeros(1, 2, 16, dtype=torch.float16), None, None, None, None)
 
 
-def test_suggest_merge_interval():
-    """The suggested M minimises the documented per-step byte model: check it
-    against the model's stationary point sqrt(2 (P - E_app) / (E_key*tiles +
-    E_val)), within the rounding to an integer, and its basic trends."""
-    import math
+def test_merge_interval_against_measured_sweep():
+    """Both merge-interval suggestions against the committed measurement on
+    MI355X (profiles/merge_interval_b256.json: B=256 H=32 d=128, one state,
+    GDN and KDA).  dl_choose_merge_interval, fed the calibrated launch times
+    recorded there, must return the M recorded as its suggestion, and whole
+    merge cycles at that M must run within 1% of the measured best M of the
+    independent sweep.  The byte model (dl_suggest_merge_interval) must
+    return its recorded M; its measured gap is larger (KDA: about 2%), so it
+    is held to 2.5%.  Invalid arguments return 0."""
+    import json
+    with open(os.path.join(ROOT, "profiles", "merge_interval_b256.json")) as f:
+        table = json.load(f)
+    for op, opi in (("gdn", GDN), ("kda", KDA)):
+        r = table[op]
+        sweep = {int(m): t for m, t in r["sweep_us_per_decode_step"].items()}
+        best = min(sweep.values())
+        assert sweep[r["measured_best_M"]] == best
+        app, mer = r["calibration_us"]["append"], r["calibration_us"]["merge"]
+        assert len(app) == 31 and len(mer) == 32
+        m_time = rsu.dl_choose_merge_interval(app, mer, 32)
+        assert m_time == r["suggested_M_from_time"], (op, m_time)
+        assert sweep[m_time] <= 1.01 * best, (op, m_time, sweep[m_time], best)
+        m_bytes = rsu.dl_suggest_merge_interval(256, 32, 128, 128, opi, BF16)
+        assert m_bytes == r["suggested_M_from_bytes"], (op, m_bytes)
+        assert sweep[m_bytes] <= 1.025 * best, (op, m_bytes, sweep[m_bytes], best)
     s = rsu.dl_suggest_merge_interval
-    for op in (GDN, KDA, RWKV6):
-        for d in (16, 32, 64, 128):
-            for dt in (F32, BF16):
-                M = s(64, 32, d, d, op, dt)
-                es = 2 if dt == BF16 else 4
-                lsz = 4 if op == GDN else 4 * d
-                e_key, e_val = d * es + lsz, d * (es if op == RWKV6 else 4)
-                tiles = d // min(d, 64)
-                P = 4 * d * d
-                m_star = math.sqrt(2 * (P - e_key - e_val) / (e_key * tiles + e_val))
-                assert 1 <= M <= 32
-                assert abs(M - min(max(m_star, 1), 32)) <= 1.0, (op, d, dt, M, m_star)
-    # a larger state defers merges longer; heavier per-key metadata merges sooner
-    assert s(64, 32, 128, 128, GDN, BF16) > s(64, 32, 32, 32, GDN, BF16)
-    assert s(64, 32, 128, 128, GDN, BF16) >= s(64, 32, 128, 128, KDA, BF16)
     assert s(0, 1, 16, 16, GDN, F32) == 0 and s(1, 1, 24, 16, GDN, F32) == 0
+    assert rsu.dl_choose_merge_interval([1.0] * 32, [2.0] * 33, 33) == 0  # max_M > 32
+    assert rsu.dl_choose_merge_interval([1.0] * 31, [float("nan")] * 32, 32) == 0
 
 
 def test_per_slot_calls_validate_before_any_launch():
