@@ -12,16 +12,20 @@ of every slot-head: (token*head)/s = B*H*M*K / region time.
 With --rotate R (default 4) the launches go round R independent states, one
 launch each in turn, as the layers of a model are stepped; the 512 MiB working
 set exceeds the 256 MB Infinity Cache, so the state streams from HBM as in
-serving.  A round of R*M launches is a whole merge cycle of every state.  The
-timed rounds are replayed from HIP graphs, one graph per window of the staged
-input pool so that the inputs keep walking the pool; K mod R further cycles
-run as direct launches, M back to back on one state.  The default workload is
-GDN B=64 H=32 d_k=d_v=128 M=8 with bf16 q/k/v and an fp32 state.
+serving.  A round of R*M launches is a whole merge cycle of every state; K
+mod R further cycles run M launches back to back on one state.  The timed
+launches are issued directly on one stream, the host running ahead of the
+GPU.  Beside them: the same rounds replayed from HIP graphs (one graph per
+window of the staged input pool; each replay starts with a gap of about 9 us
+on this ROCm, about 0.28 us per launch), and the same direct launches timed
+before the process replayed any graph (about 3% slower, a HIP runtime effect).
+The default workload is GDN B=64 H=32 d_k=d_v=128 M=8 with bf16 q/k/v and an
+fp32 state.
 
 Prints ONE JSON line: the throughput, the roofline of the step kernel
 (algorithmic bytes per launch, averaged over the merge cycle, / mean launch
-time measured with HIP events on the replay stream), the launches and merges
-timed, the direct-launch, same-GPU eager, two-stage and per-slot figures, the
+time measured with HIP events on the launch stream), the launches and merges
+timed, the graph-replayed, same-GPU eager, two-stage and per-slot figures, the
 cache-resident and 24-state figures, the other operators' workloads, and the
 fp64 CPU oracle timed on a bounded sample.
 """
@@ -216,6 +220,22 @@ def time_cycles(launch, R: int, M: int, pool: int, K: int, W: int, graphs: bool 
     t1.record(stream)
     torch.cuda.synchronize()
     return t0.elapsed_time(t1) / (K * M)
+
+
+PREWARM_ROUNDS = 64
+
+
+def prewarm(launch, R: int, M: int, pool: int, rounds: int = PREWARM_ROUNDS) -> None:
+    """Untimed whole rounds of the same launch sequence before anything is
+    timed (64 rounds: 2048 launches, about 60 ms, at the default workload), so
+    that clocks, caches and page mappings have settled."""
+    import torch
+    sp = torch.cuda.current_stream().cuda_stream
+    RM = R * M
+    for j in range(rounds):
+        for i in range(RM):
+            launch(i % R, (j * RM + i) % pool, sp)
+    torch.cuda.synchronize()
 
 
 def time_launches_bracketed(launch, R: int, M: int, pool: int, K: int, W: int) -> list:
@@ -434,10 +454,9 @@ def cpu_baseline(w, budget_s=(8.0, 5.0), pool: int = 32):
                        f"{spent1:.1f} s); input generation not timed")
 
 
-def measured_traffic():
-    """HBM bytes per launch of the step kernel (mean over a merge cycle) from
-    the committed rocprofv3 counter summary, if it was taken on the current
-    kernel source."""
+def _traffic_record():
+    """The committed rocprofv3 counter summary, if it was taken on the current
+    kernel source (else None)."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -445,19 +464,25 @@ def measured_traffic():
             sha = hashlib.sha256(f.read()).hexdigest()
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_sha256") != sha:
-        return None
-    return t.get("hbm_bytes_per_launch")
+    return t if t.get("kernel_source_sha256") == sha else None
+
+
+def measured_traffic(op: str):
+    """HBM bytes per launch of the step kernel (mean over a merge cycle) of
+    the default workload of `op`, from the committed counter summary taken on
+    the current kernel source; None otherwise."""
+    t = _traffic_record()
+    return None if t is None or op not in t else t[op].get("hbm_bytes_per_launch")
 
 
 def bench_workload(w, K, W, R, pool, with_eager=True, with_staged=True, quick=False):
     """Time workload w over K merge cycles (K*M launches; launch_order).
-    Headline: graph-replayed, timed with HIP events on the replay stream;
+    Headline: direct launches timed with HIP events on the launch stream;
     region length / (K*M) is the step kernel's mean launch duration (gaps
-    included).  Beside it: the same launches issued directly, a pass with
-    every launch bracketed by events (append and merge means), the two-stage
-    path, per-slot logs, and the eager step over the same number of launches
-    (graph-replayed too)."""
+    included).  Beside it: the same launches replayed from HIP graphs, a pass
+    with every launch bracketed by events (append and merge means), the
+    two-stage path, per-slot logs, and the eager step over the same number of
+    launches (direct and graph-replayed)."""
     import torch
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     inp = stage_inputs(w, pool, dt)
@@ -467,7 +492,16 @@ def bench_workload(w, K, W, R, pool, with_eager=True, with_staged=True, quick=Fa
     nl = K * M
     res = {}
     launch = deltalog_launcher(w, inp, sts, o)
-    ms = time_cycles(launch, R, M, pool, K, W, graphs=True)
+    prewarm(launch, R, M, pool)
+    # Order of the legs: direct launches in a process that has replayed no HIP
+    # graph yet (if none ran before this call), then the graph-replayed leg,
+    # then the direct headline.  Direct launches were measured 3% slower until
+    # the process first replays a HIP graph (any graph, even one of a single
+    # unrelated torch op; from the second timed region after it they settle),
+    # an effect of the HIP runtime whose cause is not identified here.
+    fresh = time_cycles(launch, R, M, pool, K, W, graphs=False)
+    gms = time_cycles(launch, R, M, pool, K, W, graphs=True)
+    ms = time_cycles(launch, R, M, pool, K, W, graphs=False)
     cyc_bytes = cycle_launch_bytes(w)
     res["ms_per_launch"] = ms
     res["value"] = w.BH / (ms * 1e-3)
@@ -481,9 +515,9 @@ def bench_workload(w, K, W, R, pool, with_eager=True, with_staged=True, quick=Fa
     res["modelled_step_GBs"] = round(modelled_step_bytes(w) / (ms * 1e-3) / 1e9, 1)
     if quick:  # counter runs: the headline and the eager baseline only
         with_staged = False
-    dms = time_cycles(launch, R, M, pool, K, W, graphs=False)
-    res["direct_launch"] = dict(value=round(w.BH / (dms * 1e-3), 1), us_per_launch=round(dms * 1e3, 3),
-                                achieved_GBs=round(cyc_bytes / (dms * 1e-3) / 1e9, 1))
+    res["graph_replay"] = dict(value=round(w.BH / (gms * 1e-3), 1), us_per_launch=round(gms * 1e3, 3),
+                               achieved_GBs=round(cyc_bytes / (gms * 1e-3) / 1e9, 1))
+    res["direct_first_leg_us_per_launch"] = round(fresh * 1e3, 3)
     if not quick:
         br = time_launches_bracketed(launch, R, M, pool, K, W)
         app = [x[0] for x in br if not x[2]]
@@ -492,7 +526,7 @@ def bench_workload(w, K, W, R, pool, with_eager=True, with_staged=True, quick=Fa
                                                      merge=round(1e3 * sum(mer) / max(len(mer), 1), 2))
     if R > 1 and not quick:
         one = deltalog_launcher(w, inp, sts[:1], o)
-        sms = time_cycles(one, 1, M, pool, K, W, graphs=True)
+        sms = time_cycles(one, 1, M, pool, K, W, graphs=False)
         res["single_state_value"] = round(w.BH / (sms * 1e-3), 1)
     if not quick:
         pw, pbytes, hw, hbytes = run_per_slot(w, inp, R, K, W)
@@ -513,14 +547,14 @@ def bench_workload(w, K, W, R, pool, with_eager=True, with_staged=True, quick=Fa
     if with_eager:
         bases = [base0.clone() for _ in range(R)]
         el = eager_launcher(w, inp, bases, u_dev, o)
-        ems = time_cycles(el, R, M, pool, K, W, graphs=True)
-        edms = time_cycles(el, R, M, pool, K, W, graphs=False)
+        ems = time_cycles(el, R, M, pool, K, W, graphs=False)
+        egms = time_cycles(el, R, M, pool, K, W, graphs=True)
         res["eager_same_gpu"] = dict(
             value=round(w.BH / (ems * 1e-3), 1), us_per_launch=round(ems * 1e3, 3),
             achieved_GBs=round(eager_launch_bytes(w) / (ems * 1e-3) / 1e9, 1),
             deltalog_speedup=round(ems / ms, 3),
-            direct_us_per_launch=round(edms * 1e3, 3),
-            deltalog_speedup_direct=round(edms / dms, 3))
+            graph_us_per_launch=round(egms * 1e3, 3),
+            deltalog_speedup_graph=round(egms / gms, 3))
     for st in sts:
         st.close()
     del inp, sts
@@ -532,7 +566,7 @@ def deep_rotation(w, K: int, W: int, R: int, pool: int) -> dict:
     """The headline launches over R states instead of the default 4, as a deep
     model's many layers would step them: R x (state + log) far exceeds the
     Infinity Cache, so the log entries, like the state, come from HBM.
-    DeltaLog and eager, both graph-replayed, over ceil(K / R) whole rounds
+    DeltaLog and eager, both launched directly, over ceil(K / R) whole rounds
     (R*M launches each, a whole merge cycle of every state)."""
     import torch
     K = -(-K // R) * R
@@ -540,12 +574,14 @@ def deep_rotation(w, K: int, W: int, R: int, pool: int) -> dict:
     inp = stage_inputs(w, pool, dt)
     sts, base0, u_dev = make_states(w, R, dt)
     o = torch.empty(w.B, w.H, w.dv, device="cuda")
-    ms = time_cycles(deltalog_launcher(w, inp, sts, o), R, w.M, pool, K, W, graphs=True)
+    dl = deltalog_launcher(w, inp, sts, o)
+    prewarm(dl, R, w.M, pool)
+    ms = time_cycles(dl, R, w.M, pool, K, W, graphs=False)
     for st in sts:
         st.close()
     del sts
     bases = [base0.clone() for _ in range(R)]
-    ems = time_cycles(eager_launcher(w, inp, bases, u_dev, o), R, w.M, pool, K, W, graphs=True)
+    ems = time_cycles(eager_launcher(w, inp, bases, u_dev, o), R, w.M, pool, K, W, graphs=False)
     del bases, inp
     torch.cuda.empty_cache()
     achieved = cycle_launch_bytes(w) / (ms * 1e-3) / 1e9
@@ -563,14 +599,9 @@ def pages_context(res):
     state-write cut from the committed counter summary when it was taken on
     the current kernel source."""
     cut = None
-    try:
-        with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-        with open(KERNEL_SRC, "rb") as f:
-            if t.get("kernel_source_sha256") == hashlib.sha256(f.read()).hexdigest():
-                cut = round(t["eager_write_bytes_per_step"] / t["write_bytes_per_launch"], 2)
-    except (OSError, ValueError, KeyError, ZeroDivisionError):
-        pass
+    t = _traffic_record()
+    if t is not None and "gdn" in t:
+        cut = round(t["gdn"]["eager_write_bytes_per_step"] / t["gdn"]["write_bytes_per_launch"], 2)
     eager = res.get("eager_same_gpu") or {}
     return {
         "pages_hardware": "NVIDIA H200 and RTX 4090",
@@ -641,6 +672,7 @@ def choose_merge_interval(w, pool: int, repeats: int = 3, max_M: int = 32) -> di
     sp = lambda: torch.cuda.current_stream().cuda_stream
     st = handle(max_M)
     la = deltalog_launcher(w, inp, [st], o)
+    prewarm(la, 1, max_M, pool)          # whole cycles: the log ends empty
     for i in range(max_M - 1):           # a full log of real entries
         la(0, i % pool, sp())
     app = [_fixed_n_launch_us(st, la, n, pool) for n in range(max_M - 1)]
@@ -754,8 +786,9 @@ def main():
         print(json.dumps({"choose_M": choose_merge_interval(w, pool)}), flush=True)
         return
     res = bench_workload(w, K, W, R, pool, quick=args.quick)
-    default_shape = args.workload == 1 and not args.M and not args.B and not args.H
-    res["roofline"]["traffic"] = measured_traffic() if default_shape else None
+    stock = args.workload in (1, 2, 3) and not args.M and not args.B and not args.H
+    default_shape = stock and args.workload == 1
+    res["roofline"]["traffic"] = measured_traffic(w.op) if stock else None
     log(f"{w.describe()}: {res['ms_per_launch'] * 1e3:.2f} us per decode step "
         f"({K} merge cycles, {K * w.M} launches)")
 
@@ -767,6 +800,7 @@ def main():
             others[ow.op] = dict(workload=ow.describe(), value=round(r["value"], 1),
                                  us_per_launch=round(r["ms_per_launch"] * 1e3, 3),
                                  achieved_GBs=r["roofline"]["achieved"], frac=r["roofline"]["frac"],
+                                 traffic=measured_traffic(ow.op),
                                  eager_value=r["eager_same_gpu"]["value"],
                                  deltalog_speedup=r["eager_same_gpu"]["deltalog_speedup"])
             log(f"{ow.describe()}: {r['ms_per_launch'] * 1e3:.2f} us per decode step")
@@ -805,7 +839,11 @@ def main():
         "cpu_baseline": cpu,
         "modelled_step_GBs": res["modelled_step_GBs"],
         "single_state_value": res.get("single_state_value"),
-        "direct_launch": res.get("direct_launch"),
+        "graph_replay": res.get("graph_replay"),
+        "direct_before_any_graph": dict(
+            us_per_launch=res["direct_first_leg_us_per_launch"],
+            value=round(w.BH / (res["direct_first_leg_us_per_launch"] * 1e-6), 1),
+            note="the same direct launches timed before the process replayed any HIP graph"),
         "per_slot": res.get("per_slot"),
         "two_stage": res.get("two_stage"),
         "eager_same_gpu": res.get("eager_same_gpu"),

@@ -216,9 +216,19 @@ template <typename TIn> __device__ __forceinline__ float4 cvt4(u32x4 raw)
                            __uint_as_float(raw[1] << 16), __uint_as_float(raw[1] & 0xffff0000u));
 }
 
-template <int DK, int DV> struct TileCfg {
-    static constexpr int T = DV < DL_TILE_MAX ? DV : DL_TILE_MAX;            // tile columns
-    static constexpr int NT = DK * T / 4 < DL_THREADS_MAX ? DK * T / 4 : DL_THREADS_MAX; // threads
+// The value tile of one launch.  64 columns (256 threads), except KDA's log
+// modes at d_v = 128, which take whole rows (128 columns, 512 threads): KDA's
+// per-key log-decays make each logged entry's key side (a_j and ell_j) 768
+// bytes, and the two 64-column tiles of a slot-head run on different XCDs, so
+// each would fetch it.  Whole rows read it once; measured 1% faster per step
+// at B=64 (4 rotating states) and 2.2% at B=256.  Whole rows are slower for
+// GDN, whose key side is 260 bytes, and for the eager step, which has no log.
+template <int OP, int MODE, int DK, int DV> struct TileCfg {
+    static constexpr bool WIDE = OP == KDA && MODE != EAGER && DV == 128;
+    static constexpr int TMAX = WIDE ? 128 : DL_TILE_MAX;
+    static constexpr int THR = WIDE ? 512 : DL_THREADS_MAX;
+    static constexpr int T = DV < TMAX ? DV : TMAX;                  // tile columns
+    static constexpr int NT = DK * T / 4 < THR ? DK * T / 4 : THR;  // threads
     static constexpr int LPR = T / 4;     // lanes per row
     static constexpr int RPP = NT / LPR;  // rows per pass of the workgroup
     static constexpr int P = DK / RPP;    // rows per lane
@@ -285,7 +295,11 @@ __global__ __launch_bounds__(256) void replay_prep_kernel(StepArgs a)
     constexpr int KPL = (DK + 63) / 64; // keys per lane
     constexpr int EB = 8;               // log entries whose loads are issued together
     const int lane = threadIdx.x & 63;
-    const int sh = blockIdx.x * 4 + (threadIdx.x >> 6);
+    // the wave's slot-head, uniform over the wave: read from the first lane so
+    // that the compiler keeps it (and the buffer resources built from it) in
+    // scalar registers; otherwise every buffer load becomes a loop over the
+    // lanes' resources, each iteration waiting for its load
+    const int sh = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (sh >= a.BH)
         return; // whole wave leaves together
     const int n = a.n, M = a.M;
@@ -421,10 +435,10 @@ template <typename TIn> __host__ __device__ constexpr int min_waves(int mode)
 //                    merge workgroups.
 // Merging launches end with the fold and the single dense write.
 template <int OP, typename TIn, int DK, int DV, int MODE>
-__global__ __launch_bounds__((TileCfg<DK, DV>::NT)) __attribute__((amdgpu_waves_per_eu(min_waves<TIn>(MODE))))
+__global__ __launch_bounds__((TileCfg<OP, MODE, DK, DV>::NT)) __attribute__((amdgpu_waves_per_eu(min_waves<TIn>(MODE))))
 void step_kernel(StepArgs a)
 {
-    using C = TileCfg<DK, DV>;
+    using C = TileCfg<OP, MODE, DK, DV>;
     constexpr int T = C::T, NT = C::NT, LPR = C::LPR, RPP = C::RPP, P = C::P;
     constexpr int NTILE = C::NTILE, NW = C::NW;
     constexpr bool DELTA = OP != RWKV6;
@@ -1026,7 +1040,7 @@ hipError_t launch_prep(int dtype, int dk, const StepArgs &a, hipStream_t st)
 template <int OP, typename TIn, int DK, int DV, int MODE>
 hipError_t launch_step_t(const StepArgs &a, hipStream_t st)
 {
-    using C = TileCfg<DK, DV>;
+    using C = TileCfg<OP, MODE, DK, DV>;
     // per-slot launches size LDS for the longest log and may cover one slot
     const int slot_heads = (MODE == SFOLD && a.slot >= 0) ? a.H : a.BH;
     const int n_lds = (MODE == SSTEP || MODE == SFOLD) ? a.M - 1 : a.n;
