@@ -216,15 +216,19 @@ template <typename TIn> __device__ __forceinline__ float4 cvt4(u32x4 raw)
                            __uint_as_float(raw[1] << 16), __uint_as_float(raw[1] & 0xffff0000u));
 }
 
-// The value tile of one launch.  64 columns (256 threads), except KDA's log
-// modes at d_v = 128, which take whole rows (128 columns, 512 threads): KDA's
-// per-key log-decays make each logged entry's key side (a_j and ell_j) 768
-// bytes, and the two 64-column tiles of a slot-head run on different XCDs, so
-// each would fetch it.  Whole rows read it once; measured 1% faster per step
-// at B=64 (4 rotating states) and 2.2% at B=256.  Whole rows are slower for
-// GDN, whose key side is 260 bytes, and for the eager step, which has no log.
+// The value tile of one launch.  64 columns (256 threads), except where
+// whole rows (128 columns, 512 threads, d_v = 128) measured faster:
+//   - KDA's log modes: KDA's per-key log-decays make each logged entry's key
+//     side (a_j and ell_j) 768 bytes, and the two 64-column tiles of a
+//     slot-head run on different XCDs, so each would fetch it; whole rows read
+//     it once (1% faster per step at B=64 with 4 rotating states, 2.2% at
+//     B=256);
+//   - GDN's merge launches (0.4% per step).
+// GDN's appends (a 260-byte key side) and every eager step run faster on
+// 64-column tiles.
 template <int OP, int MODE, int DK, int DV> struct TileCfg {
-    static constexpr bool WIDE = OP == KDA && MODE != EAGER && DV == 128;
+    static constexpr bool WIDE = DV == 128 && ((OP == KDA && MODE != EAGER) ||
+                                               (OP == GDN && (MODE == MERGE || MODE == FMERGE)));
     static constexpr int TMAX = WIDE ? 128 : DL_TILE_MAX;
     static constexpr int THR = WIDE ? 512 : DL_THREADS_MAX;
     static constexpr int T = DV < TMAX ? DV : TMAX;                  // tile columns
