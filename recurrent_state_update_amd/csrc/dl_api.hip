@@ -569,7 +569,10 @@ int dl_suggest_merge_interval(int B, int H, int d_k, int d_v, dl_op op, dl_dtype
     const double lsz = op == DL_OP_GDN ? 4.0 : 4.0 * d_k;
     const double e_key = d_k * es + lsz;
     const double e_val = d_v * (op == DL_OP_RWKV6 ? es : 4.0);
-    const double tiles = d_v / (double)(d_v < 64 ? d_v : 64);
+    // value tiles per slot-head in an append launch, each re-reading the key
+    // side: 64-column tiles, except KDA at d_v = 128, whose logged modes take
+    // whole rows (as the step kernel does)
+    const double tiles = (op == DL_OP_KDA && d_v == 128) ? 1.0 : d_v / (double)(d_v < 64 ? d_v : 64);
     int best = 1;
     double best_bytes = 0.0;
     for (int M = 1; M <= 32; ++M) {

@@ -153,7 +153,7 @@ def test_merge_interval_against_measured_sweep():
     recorded there, must return the M recorded as its suggestion, and whole
     merge cycles at that M must run within 1% of the measured best M of the
     independent sweep.  The byte model (dl_suggest_merge_interval) must
-    return its recorded M; its measured gap is larger (KDA: about 2%), so it
+    return its recorded M; its measured gap is larger (KDA: about 1.2%), so it
     is held to 2.5%.  Invalid arguments return 0."""
     import json
     with open(os.path.join(ROOT, "profiles", "merge_interval_b256.json")) as f:
