@@ -48,7 +48,8 @@
  *                  the two-stage path's per-step coefficients and the per-slot
  *                  log phases; contents need no initialisation
  * Supported shapes: d_k, d_v in {16, 32, 64, 128}; 1 <= M <= 32; B, H >= 1
- * with B*H*d_k*d_v < 2^31.  All B slots step in lockstep (one shared log
+ * with B*H*d_k*d_v < 2^33 (a state of up to 32 GiB per handle; larger shapes
+ * return DL_E_SHAPE).  All B slots step in lockstep (one shared log
  * length) unless per-slot logs are enabled (see the end of this file).
  *
  * Errors and ownership.  Every call returns a dl_status and never aborts or

@@ -76,7 +76,12 @@ dl_status check_shape(int B, int H, int dk, int dv, int M, int op, int dtype)
         return DL_E_INVALID;
     if (!dim_ok(dk) || !dim_ok(dv))
         return DL_E_SHAPE;
-    if ((long long)B * H * dk * dv >= (1LL << 31))
+    // Every launch dispatches at most d_k*d_v/4 work-items per slot-head
+    // (each step-kernel lane holds at least 4 state elements; ReplayPrep runs
+    // 64, and d_k*d_v >= 256), and a dispatch counts its work-items in 32
+    // bits: below 2^33 state elements (a 32 GiB fp32 state) every launch
+    // stays under 2^31 of them.  Device offsets are 64-bit throughout.
+    if ((long long)B * H * dk * dv >= (1LL << 33))
         return DL_E_SHAPE;
     return DL_OK;
 }

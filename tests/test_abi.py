@@ -77,7 +77,17 @@ def test_create_validation():
     assert _create(op=RWKV6, u=None)[0] == INVALID
     assert _create(base=BASE + 4)[0] == ALIGN
     assert _create(ws=WS + 16)[0] == ALIGN
-    assert _create(B=1 << 16, H=1 << 8, dk=128, dv=128)[0] == SHAPE  # state >= 2^31 elements
+    assert _create(B=1 << 16, H=1 << 8, dk=128, dv=128)[0] == SHAPE  # state >= 2^33 elements
+    # the limit itself: 2^33 state elements are refused, one slot-head fewer
+    # is accepted (base and workspace far apart: the base alone spans 32 GiB)
+    far = dict(base=0x100000000000, ws=0x200000000000)
+    assert _create(B=1 << 19, H=1, dk=128, dv=128, **far)[0] == SHAPE
+    assert _create(B=1 << 13, H=1 << 12, dk=16, dv=16, **far)[0] == SHAPE
+    st, h = _create(B=(1 << 19) - 1, H=1, dk=128, dv=128, **far)
+    assert st == OK and h
+    rsu.dl_state_destroy(h)
+    assert rsu.dl_workspace_bytes(1 << 19, 1, 128, 128, 2, GDN, BF16) == 0
+    assert rsu.dl_workspace_bytes((1 << 19) - 1, 1, 128, 128, 2, GDN, BF16) > 0
     st = _lib.dl_state_create(1, 1, 16, 16, 4, GDN, F32, BASE, WS, None, None)
     assert st == INVALID  # NULL out-pointer
     st, h = _create()

@@ -385,14 +385,15 @@ def test_full_size_graph_replay(orc, wid):
 
 @needs_gpu
 def test_largest_state_the_abi_accepts(orc):
-    """The largest state below the 2^31-element limit at d=128: B*H = 131071
-    slot-heads (8 GiB of fp32 state), GDN bf16, M=2, three steps (a merge and a
+    """The largest state below the 2^33-element limit at d=128: B*H = 524287
+    slot-heads (32 GiB of fp32 state, so the last slot-heads lie past 2^31
+    elements and 2^32 bytes), GDN bf16, M=2, three steps (a merge and a
     pending log).  The base is zero except on 48 sampled slot-heads (first and
     last included), whose seeded initial states and every output are checked
     against the oracle, with the base after the final forced merge."""
     import recurrent_state_update_amd as rsu
-    B, H, d, M = 131071, 1, 128, 2
-    assert B * H * d * d < 2**31 and (B + 1) * H * d * d >= 2**31
+    B, H, d, M = 524287, 1, 128, 2
+    assert B * H * d * d < 2**33 and (B + 1) * H * d * d >= 2**33
     w = synth.Workload(19, "gdn", B, H, d, d, M, 3, "bf16")
     idx = sample_slot_heads(B * H, 48, seed=19)
     X0_rows = synth.initial(w.with_(B=len(idx)))[0].reshape(len(idx), d, d)  # seeded rows for the sample
