@@ -331,17 +331,25 @@ __global__ __launch_bounds__(256) void replay_prep_kernel(StepArgs a)
     load_batch(n - 1); // first batch of entry loads, ahead of everything else
     const rsrc_t qr = make_rsrc(static_cast<const TIn *>(a.q) + (long)sh * DK, DK * sizeof(TIn));
     const rsrc_t kr = make_rsrc(static_cast<const TIn *>(a.k) + (long)sh * DK, DK * sizeof(TIn));
-    float qv[KPL], kv[KPL], ell[KPL], sfx[KPL];
+    const rsrc_t ur = make_rsrc(a.u + (long)(sh % a.H) * DK, OP == RWKV6 ? DK * 4 : 0);
+    float qv[KPL], kv[KPL], uv[KPL], ell[KPL], sfx[KPL];
 #pragma unroll
     for (int c = 0; c < KPL; ++c) {
         const int i = lane + 64 * c;
         const unsigned ei = i < DK ? (unsigned)i : kSkipElem;
         qv[c] = buf_ld_in<TIn>(qr, ei);
         kv[c] = buf_ld_in<TIn>(kr, ei);
+        uv[c] = OP == RWKV6 ? buf_ld_in<float>(ur, ei) : 0.f; // RWKV6's bonus u
         ell[c] = floor_log_decay(OP == GDN ? a.ld[sh] : (i < DK ? a.ld[(long)sh * DK + i] : 0.f));
         sfx[c] = 0.f; // running suffix sum of the logged per-key log-decays
     }
     float gsfx = 0.f; // GDN: the same for its scalar log-decays
+    // Lane m keeps entry m's coefficients (M <= 32 lanes), stored once after
+    // the walk.  A store inside the walk would sit in a lane-0 branch, and the
+    // wait for the next entry's loads would then also wait for that store
+    // (the memory counter counts both, and the branch hides how many are in
+    // flight): one store round trip per entry.
+    float cq_m = 0.f, ck_m = 0.f;
 
     float *coef = a.coef + (long)sh * a.cstride;
     for (int top = n - 1; top >= 0; top -= EB) {
@@ -376,13 +384,9 @@ __global__ __launch_bounds__(256) void replay_prep_kernel(StepArgs a)
             sq = wave_sum_from<1>(sq);
             if (OP != RWKV6)
                 sk = wave_sum_from<1>(sk);
-            sq *= g;
-            sk *= g;
-            if (lane == 0) {
-                coef[m] = sq;
-                if (OP != RWKV6)
-                    coef[M + m] = sk;
-            }
+            // every lane holds the sums; lane m keeps them
+            cq_m = lane == m ? sq * g : cq_m;
+            ck_m = lane == m ? sk * g : ck_m;
         }
     }
 
@@ -391,13 +395,13 @@ __global__ __launch_bounds__(256) void replay_prep_kernel(StepArgs a)
     for (int c = 0; c < KPL; ++c) {
         const int i = lane + 64 * c;
         if (i < DK)
-            kap += OP == RWKV6 ? qv[c] * a.u[(long)(sh % a.H) * DK + i] * kv[c] : qv[c] * kv[c];
+            kap += OP == RWKV6 ? qv[c] * uv[c] * kv[c] : qv[c] * kv[c];
     }
     kap = wave_sum_from<1>(kap);
-    if (lane == 0)
-        coef[2 * M] = kap;
 
-    // key-side append of entry n
+    // Every store last, after every load has been used (a wait for a load
+    // issued before a store would also wait for the store).  The key-side
+    // append of entry n first: it is the last use of the step's log-decay.
     TIn *an = static_cast<TIn *>(a.alog) + ((long)sh * M + n) * DK;
 #pragma unroll
     for (int c = 0; c < KPL; ++c) {
@@ -410,6 +414,13 @@ __global__ __launch_bounds__(256) void replay_prep_kernel(StepArgs a)
     }
     if (OP == GDN && lane == 0)
         L[n] = ell[0];
+    if (lane < n) {
+        coef[lane] = cq_m;
+        if (OP != RWKV6)
+            coef[M + lane] = ck_m;
+    }
+    if (lane == 0)
+        coef[2 * M] = kap;
 }
 
 // Waves per SIMD the compiler must leave room for: 8 (64 VGPRs) for the
