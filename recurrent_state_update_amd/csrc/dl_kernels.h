@@ -532,7 +532,7 @@ void step_kernel(StepArgs a)
     float *Bt = dyn + kRowTables * TS;         // [nb][T] value-side factors of this tile
     float *F = Bt + nb * T;                    // [kr][DK] per-key table: logged decays, turned
                                                // into suffix sums in place, then fold rows
-    float *cf = F + kr * DK;                   // [2n+1] c^q, c^k, kappa (LOGGED)
+    float *cf = F + kr * DK;                   // [2n+1] (c^q_m, c^k_m) pairs, kappa (LOGGED)
     float *gsum = cf + (LOGGED ? 2 * n + 1 : 0); // GDN: [n] suffix sums S_m
     float *junk = dyn + ((kRowTables * TS + nb * T + kr * DK + (LOGGED ? 2 * n + 1 : 0) +
                           (OP == GDN && mode_has_log(MODE) ? n : 0) + 3) & ~3);
@@ -670,8 +670,11 @@ void step_kernel(StepArgs a)
         if (wave == 0 && lane < n)
             gsum[lane] = gS;
     }
-    // GDN: Lam' (a standalone fold: Lam_{n-1}); applied as a scalar after the sums
+    // GDN: Lam' (a standalone fold: Lam_{n-1}) and e^{Lam'}, which scales the
+    // read weights (so the column sums need no scaling afterwards) and the
+    // fold's base factor
     const float gnew = gT + gell;
+    const float egnew = OP == GDN ? expf(gnew) : 1.f;
     // Per-row tables that depend on T = Lam_{n-1,i}: read weights, fold base
     // factor and offsets.  T is 0 for an empty log; GDN applies its scalar T
     // after the sums, so its tables never need it.
@@ -679,9 +682,9 @@ void step_kernel(StepArgs a)
         const int i = tid + j * NT;
         const float rd = DELTA ? mell[j] : 0.f; // the delta rule reads the decayed state
         float wq, wk = 0.f;
-        if (OP == GDN) {
-            wq = mq[j];
-            wk = mk[j];
+        if (OP == GDN) { // the read's scalar e^{Lam'}, one factor per slot-head
+            wq = egnew * mq[j];
+            wk = egnew * mk[j];
         } else if (OP == KDA) {
             const float e = expf(Tr + rd);
             wq = e * mq[j];
@@ -743,7 +746,8 @@ void step_kernel(StepArgs a)
             shard_store(s, shard_load(s));
     }
     if (STAGED)
-        (tid < 2 * n + 1 ? cf + tid : junk)[0] = __uint_as_float(cst);
+        (tid < 2 * n + 1 ? cf + (tid < n ? 2 * tid : tid < 2 * n ? 2 * (tid - n) + 1 : 2 * n) : junk)[0] =
+            __uint_as_float(cst);
     __syncthreads();
 
     // ---- 2b. KDA, RWKV6: suffix sums of the logged decays, key by key in
@@ -803,8 +807,8 @@ void step_kernel(StepArgs a)
             if (DELTA)
                 sk = wave_sum_from<1>(sk);
             if (lane == 0) {
-                cf[m] = g * sq;
-                cf[n + m] = g * sk;
+                cf[2 * m] = g * sq;
+                cf[2 * m + 1] = g * sk;
             }
         };
         // entries wave, wave + NW, ... below NW*EW: loaded ahead of the tile
@@ -906,25 +910,21 @@ void step_kernel(StepArgs a)
                 y[c] += red[w][c4][c];
             kap += red[w][0][8];
         }
-        if (OP == GDN) {
-            const float g = expf(gnew);
-#pragma unroll
-            for (int c = 0; c < 8; ++c)
-                y[c] *= g;
-        }
         // the log's replay terms sum_m c_m b_m, added onto the base's column
-        // sums (q side into y[0..3], k side into y[4..7])
+        // sums (q side into y[0..3], k side into y[4..7]); an entry's two
+        // coefficients sit side by side, so each entry costs one LDS round
+        // trip (its coefficient pair and its value-side factors together)
         if (LOGGED) {
 #pragma unroll 1
             for (int m = grp; m < n; m += G) {
                 const float4 b = *reinterpret_cast<const float4 *>(Bt + m * T + 4 * c4);
+                const float2 cqk = *reinterpret_cast<const float2 *>(cf + 2 * m);
                 const float bs[4] = {b.x, b.y, b.z, b.w};
-                const float cq = cf[m], ck = cf[n + m];
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
-                    y[c] = fmaf(cq, bs[c], y[c]);
+                    y[c] = fmaf(cqk.x, bs[c], y[c]);
                     if (DELTA)
-                        y[4 + c] = fmaf(ck, bs[c], y[4 + c]);
+                        y[4 + c] = fmaf(cqk.y, bs[c], y[4 + c]);
                 }
             }
         }
@@ -992,7 +992,7 @@ void step_kernel(StepArgs a)
     // --------------------------------------- 7. fold and write the tile once
     if (writes) { // uniform over the workgroup
         __syncthreads();
-        const float gs = OP == GDN ? expf(gnew) : 1.f;
+        const float gs = egnew;
 #pragma unroll
         for (int p = 0; p < P; ++p) {
             const float bf = OP == GDN ? gs : Rf[r0 + p * RPP];
