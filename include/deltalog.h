@@ -241,8 +241,9 @@ int dl_choose_merge_interval(const double *append_us, const double *merge_us, in
 dl_status dl_state_enable_slots(dl_state *s, void *stream);
 
 /* Admit a new request into `slot` (also one released before): drop the
- * slot's pending log without folding it.  The caller writes the request's initial state into the slot's
- * rows of `base` ([slot, 0..H)) before the next step (stream-ordered). */
+ * slot's pending log without folding it.  The caller writes the request's
+ * initial state into the slot's rows of `base` ([slot, 0..H)) before the next
+ * step (stream-ordered). */
 dl_status dl_slot_admit(dl_state *s, int slot, void *stream);
 
 /* Fold the pending entries of one slot into its rows of `base` (which then
