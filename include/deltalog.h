@@ -199,10 +199,11 @@ dl_status dl_eager_step(dl_op op, int B, int H, int d_k, int d_v, dl_dtype in_dt
  *   bytes(M) = P (1 + 1/M)                  base read every step, write per merge
  *            + (M-1)/2 (E_key * tiles + E_val)   replay of the logged entries
  *            + (M-1)/M E_app                 appended entry (none on the merge)
+ *            + (M-1)/M E_key (tiles_m - tiles)   the merge's extra key-side reads
  * with P = 4 d_k d_v, E_key = a_j + log-decay bytes (re-read by each value
- * tile of an append launch: d_v/min(d_v, 64) tiles, one for KDA at
- * d_v = 128, whose logged modes take whole rows), E_val = b_j bytes,
- * E_app = E_key + E_val.
+ * tile: tiles_m = d_v/min(d_v, 64) tiles for a merge, and as many for an
+ * append except KDA at d_v = 128, whose appends take whole rows: tiles = 1),
+ * E_val = b_j bytes, E_app = E_key + E_val.
  * Returns 0 for invalid arguments. */
 int dl_suggest_merge_interval(int B, int H, int d_k, int d_v, dl_op op, dl_dtype in_dtype);
 

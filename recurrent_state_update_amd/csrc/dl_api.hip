@@ -574,15 +574,17 @@ int dl_suggest_merge_interval(int B, int H, int d_k, int d_v, dl_op op, dl_dtype
     const double lsz = op == DL_OP_GDN ? 4.0 : 4.0 * d_k;
     const double e_key = d_k * es + lsz;
     const double e_val = d_v * (op == DL_OP_RWKV6 ? es : 4.0);
-    // value tiles per slot-head in an append launch, each re-reading the key
-    // side: 64-column tiles, except KDA at d_v = 128, whose logged modes take
-    // whole rows (as the step kernel does)
-    const double tiles = (op == DL_OP_KDA && d_v == 128) ? 1.0 : d_v / (double)(d_v < 64 ? d_v : 64);
+    // value tiles per slot-head, each re-reading the key side: 64-column
+    // tiles, except KDA's appends at d_v = 128, which take whole rows (as the
+    // step kernel does); a merge always takes 64-column tiles
+    const double tiles_merge = d_v / (double)(d_v < 64 ? d_v : 64);
+    const double tiles = (op == DL_OP_KDA && d_v == 128) ? 1.0 : tiles_merge;
     int best = 1;
     double best_bytes = 0.0;
     for (int M = 1; M <= 32; ++M) {
         const double bytes = P * (1.0 + 1.0 / M) + 0.5 * (M - 1) * (e_key * tiles + e_val) +
-                             (double)(M - 1) / M * (e_key + e_val);
+                             (double)(M - 1) / M * (e_key + e_val) +
+                             (tiles_merge - tiles) * (double)(M - 1) / M * e_key; // the merge's extra reads
         if (M == 1 || bytes < best_bytes) {
             best = M;
             best_bytes = bytes;

@@ -216,22 +216,27 @@ template <typename TIn> __device__ __forceinline__ float4 cvt4(u32x4 raw)
                            __uint_as_float(raw[1] << 16), __uint_as_float(raw[1] & 0xffff0000u));
 }
 
-// The value tile of one launch.  64 columns (256 threads), except where
-// whole rows (128 columns, 512 threads, d_v = 128) measured faster:
-//   - KDA's log modes: KDA's per-key log-decays make each logged entry's key
-//     side (a_j and ell_j) 768 bytes, and the two 64-column tiles of a
-//     slot-head run on different XCDs, so each would fetch it; whole rows read
-//     it once (1% faster per step at B=64 with 4 rotating states, 2.2% at
-//     B=256);
-//   - GDN's merge launches (0.4% per step).
-// GDN's appends (a 260-byte key side) and every eager step run faster on
-// 64-column tiles.  THREADS, when set, asks for that many threads per tile
-// (the eager step's second tiling, chosen by batch size at launch).
+// The value tile of one launch: 64 columns, with 256 threads (8 rows per lane
+// at d_k = 128) or 512 (4 rows per lane), except where whole rows (128
+// columns, 512 threads, d_v = 128) measured faster.  Per decode step, with 4
+// rotating states:
+//   - KDA's appends, per-slot steps and standalone folds take whole rows:
+//     KDA's per-key log-decays make each logged entry's key side (a_j and
+//     ell_j) 768 bytes, and the two 64-column tiles of a slot-head run on
+//     different XCDs, so each would fetch it; whole rows read it once (1%
+//     faster at B=64, 2.2% at B=256);
+//   - merges (every operator) take 64-column tiles with 512 threads: 0.1-0.4%
+//     faster than whole rows at B=64, 1.1-1.5% at B=256 (GDN, KDA);
+//   - GDN's appends (a 260-byte key side) take 64-column tiles with 256
+//     threads; 512 threads are 0.1-0.3 us slower;
+//   - the eager step takes 64-column tiles, with 512 threads at d_k = 128 up
+//     to a batch size chosen at launch (THREADS), 256 beyond.
+// THREADS, when set, asks for that many threads per tile.
 template <int OP, int MODE, int DK, int DV, int THREADS = 0> struct TileCfg {
-    static constexpr bool WIDE = DV == 128 && ((OP == KDA && MODE != EAGER) ||
-                                               (OP == GDN && (MODE == MERGE || MODE == FMERGE)));
+    static constexpr bool MERGES = MODE == MERGE || MODE == FMERGE;
+    static constexpr bool WIDE = DV == 128 && OP == KDA && MODE != EAGER && !MERGES;
     static constexpr int TMAX = WIDE ? 128 : DL_TILE_MAX;
-    static constexpr int THR = THREADS ? THREADS : WIDE ? 512 : DL_THREADS_MAX;
+    static constexpr int THR = THREADS ? THREADS : (WIDE || (MERGES && DV >= 64)) ? 512 : DL_THREADS_MAX;
     static constexpr int T = DV < TMAX ? DV : TMAX;                  // tile columns
     static constexpr int NT = DK * T / 4 < THR ? DK * T / 4 : THR;  // threads
     static constexpr int LPR = T / 4;     // lanes per row
