@@ -26,8 +26,10 @@ Prints ONE JSON line: the throughput, the roofline of the step kernel
 (algorithmic bytes per launch, averaged over the merge cycle, / mean launch
 time measured with HIP events on the launch stream), the launches and merges
 timed, the graph-replayed, same-GPU eager, two-stage and per-slot figures, the
-cache-resident and 24-state figures, the other operators' workloads, and the
-fp64 CPU oracle timed on a bounded sample.
+cache-resident and 24-state figures, the HBM rate of the step kernel's own
+access pattern on the state (pattern_ceiling: context beside the 8 TB/s peak),
+the other operators' workloads, and the fp64 CPU oracle timed on a bounded
+sample.
 """
 from __future__ import annotations
 
@@ -559,6 +561,8 @@ def bench_workload(w, K, W, R, pool, with_eager=True, with_staged=True, quick=Fa
         st.close()
     del inp, sts
     torch.cuda.empty_cache()
+    if not quick:
+        res["pattern_ceiling"] = pattern_ceiling(w, R, ms)
     return res
 
 
@@ -589,6 +593,79 @@ def deep_rotation(w, K: int, W: int, R: int, pool: int) -> dict:
                 us_per_launch=round(ms * 1e3, 3), achieved_GBs=round(achieved, 1),
                 frac=round(achieved / PEAK_HBM_GBS, 4), eager_us_per_launch=round(ems * 1e3, 3),
                 deltalog_speedup=round(ems / ms, 3))
+
+
+def pattern_ceiling(w, R: int, ms_step: float) -> dict | None:
+    """The HBM rate that the step kernel's own access pattern on the state
+    reaches on this GPU, as context for the roofline (whose peak stays the
+    published 8 TB/s): R rotating states of the workload's shape, each launch
+    a pass over every value tile in the step kernel's block order, lane layout
+    and load hint (libdlceiling, csrc/dl_ceiling.hip), either a pure read (an
+    append's state traffic) or an in-place read and rewrite (a merge's),
+    each timed back to back on its own; then whole merge cycles of such
+    passes in the benchmark's launch order (the R states in turn, every M-th
+    pass of a state a rewrite), the time the state traffic alone takes in
+    that pattern.  `step_vs_pattern` is the DeltaLog step's achieved rate of
+    algorithmic bytes (state, log, inputs and outputs) over that cycle's rate
+    of state bytes."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "recurrent_state_update_amd", "libdlceiling.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built (run __graft_entry__.build())")
+    lib = ctypes.CDLL(path)
+    lib.dlc_sink_floats.argtypes = [ctypes.c_int] * 3
+    lib.dlc_sink_floats.restype = ctypes.c_long
+    lib.dlc_tile_pass.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p]
+    lib.dlc_tile_pass.restype = ctypes.c_int
+    nsink = lib.dlc_sink_floats(w.BH, w.dk, w.dv)
+    if nsink == 0:
+        return None
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    states = [torch.randn(w.BH * w.dk * w.dv, device="cuda", generator=g) for _ in range(R)]
+    sink = torch.empty(nsink, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    M = w.M
+
+    def passes(kind, count):
+        # kind 0: reads, 1: rewrites, 2: merge cycles (launch i: state i % R,
+        # the M-th pass of each state's cycle a rewrite)
+        for i in range(count):
+            write = kind if kind < 2 else int((i // R) % M == M - 1)
+            if lib.dlc_tile_pass(states[i % R].data_ptr(), w.BH, w.dk, w.dv, write, sink.data_ptr(),
+                                 float("nan"), sp) != 0:
+                raise RuntimeError("dlc_tile_pass failed")
+
+    def timed(kind, count):
+        passes(kind, count // 4)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        passes(kind, count)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) * 1e3 / count
+
+    state_bytes = 4 * w.BH * w.dk * w.dv
+    out = dict(rotate_states=R)
+    for kind, name in ((0, "read"), (1, "read_write")):
+        us = timed(kind, 64 * R)
+        out[name] = dict(us_per_launch=round(us, 2), GBs=round(state_bytes * (1 + kind) / us / 1e3, 1))
+    cyc_us = timed(2, 16 * R * M)
+    del states, sink
+    torch.cuda.empty_cache()
+    pattern_gbs = state_bytes * (1 + 1 / M) / cyc_us / 1e3
+    step_gbs = cycle_launch_bytes(w) / (ms_step * 1e-3) / 1e9
+    out["cycle_us_per_launch"] = round(cyc_us, 2)
+    out["cycle_GBs"] = round(pattern_gbs, 1)
+    out["cycle_frac_of_peak"] = round(pattern_gbs / PEAK_HBM_GBS, 4)
+    out["step_vs_pattern"] = round(step_gbs / pattern_gbs, 4)
+    return out
 
 
 def pages_context(res):
@@ -802,7 +879,9 @@ def main():
                                  achieved_GBs=r["roofline"]["achieved"], frac=r["roofline"]["frac"],
                                  traffic=measured_traffic(ow.op),
                                  eager_value=r["eager_same_gpu"]["value"],
-                                 deltalog_speedup=r["eager_same_gpu"]["deltalog_speedup"])
+                                 deltalog_speedup=r["eager_same_gpu"]["deltalog_speedup"],
+                                 pattern_cycle_GBs=(r.get("pattern_ceiling") or {}).get("cycle_GBs"),
+                                 step_vs_pattern=(r.get("pattern_ceiling") or {}).get("step_vs_pattern"))
             log(f"{ow.describe()}: {r['ms_per_launch'] * 1e3:.2f} us per decode step")
 
     deep = None
@@ -847,6 +926,7 @@ def main():
         "per_slot": res.get("per_slot"),
         "two_stage": res.get("two_stage"),
         "eager_same_gpu": res.get("eager_same_gpu"),
+        "pattern_ceiling": res.get("pattern_ceiling"),
         "deep_rotation": deep,
         "other_workloads": others or None,
         "pages_context": pages_context(res),

@@ -1,5 +1,6 @@
 """Build step of libdeltalog: compiles the HIP sources for gfx950 with hipcc
-and links ``libdeltalog.so`` next to this file.
+and links ``libdeltalog.so`` next to this file (and ``libdlceiling.so``, the
+benchmark's pattern-ceiling helper, from ``csrc/dl_ceiling.hip``).
 
     python recurrent_state_update_amd/_build.py
 
@@ -21,6 +22,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdeltalog.so")
+# the benchmark's pattern-ceiling helper, a library of its own (not part of
+# the decode path)
+CEILING_LIB = os.path.join(PKG, "libdlceiling.so")
 SOURCES = ["dl_api.hip", "dl_device.hip", "dl_gdn.hip", "dl_kda.hip", "dl_rwkv6.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -62,5 +66,18 @@ def build(defines: list[str] | None = None, out: str = LIB, build_dir: str | Non
     return out
 
 
+def build_ceiling(out: str = CEILING_LIB) -> str:
+    """Compile and link libdlceiling.so (csrc/dl_ceiling.hip), which bench.py
+    loads to measure the HBM rate of the step kernel's own access pattern."""
+    tmp = out + ".tmp"
+    cmd = [HIPCC, *CFLAGS, "-shared", os.path.join(CSRC, "dl_ceiling.hip"), "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on dl_ceiling.hip:\n{r.stderr}")
+    os.replace(tmp, out)
+    return out
+
+
 if __name__ == "__main__":
     print(build(defines=sys.argv[1:]))
+    print(build_ceiling())
