@@ -62,51 +62,61 @@ def _sizes(w):
     es = 2 if w.dtype == "bf16" else 4
     delta = w.op != "rwkv6"
     return dict(P=4 * w.dk * w.dv, es=es, delta=delta, bsz=4 if delta else es,
-                lsz=4 if w.op == "gdn" else 4 * w.dk)
+                lsz=4 if w.op == "gdn" else 4 * w.dk,
+                # RWKV6's bonus u [H, d_k] fp32: one copy per head, shared by
+                # the B slots, so counted once per launch (not per slot-head)
+                u=0 if delta else 4 * w.H * w.dk)
 
 
-def step_launch_bytes(w, n: int, merge: bool) -> int:
-    """Algorithmic HBM bytes of one launch of the one-launch step kernel over
-    all B*H slot-heads, n = log entries before the step.  Per slot-head:
-    base read P (+ base write P on a merge); the n logged entries' a_j, Lam_j
-    and b_j; q, k, v, beta, log-decay (+ u for RWKV6); o; and on append steps
-    the appended a_n, Lam_n, b_n."""
+def slot_head_bytes(w, n: int, merge: bool) -> int:
+    """Algorithmic HBM bytes of one slot-head in one launch of the one-launch
+    step kernel, n = log entries before the step: base read P (+ base write P
+    on a merge); the n logged entries' a_j, Lam_j and b_j; q, k, v, beta
+    (delta rule), log-decay; o; and on append steps the appended a_n, Lam_n,
+    b_n."""
     z = _sizes(w)
     dk, dv = w.dk, w.dv
     per = z["P"] + n * (dk * z["es"] + z["lsz"] + dv * z["bsz"])
-    per += 2 * dk * z["es"] + dv * z["es"] + (4 if z["delta"] else 4 * dk) + z["lsz"]
+    per += 2 * dk * z["es"] + dv * z["es"] + (4 if z["delta"] else 0) + z["lsz"]
     per += dv * 4
     if merge:
         per += z["P"]
     else:
         per += dk * z["es"] + z["lsz"] + dv * z["bsz"]
-    return per * w.BH
+    return per
+
+
+def step_launch_bytes(w, n: int, merge: bool) -> int:
+    """Algorithmic HBM bytes of one launch over all B*H slot-heads at log
+    length n: slot_head_bytes for each, plus RWKV6's bonus u [H, d_k] once."""
+    return slot_head_bytes(w, n, merge) * w.BH + _sizes(w)["u"]
 
 
 def cycle_launch_bytes(w) -> float:
     """Mean algorithmic bytes per launch over one merge cycle (log lengths
     0..M-1, the last launch merging).  Equals the per-step traffic model
-    P(1 + 1/M) + E((M-1)/M + (M-1)/2) + I per slot-head (modelled_step_bytes)."""
+    P(1 + 1/M) + E((M-1)/M + (M-1)/2) + I per slot-head, plus u once
+    (modelled_step_bytes)."""
     return sum(step_launch_bytes(w, n, n + 1 == w.M) for n in range(w.M)) / w.M
 
 
 def eager_launch_bytes(w) -> int:
-    """Eager step: read and write the base, inputs, o."""
+    """Eager step: read and write the base, inputs, o (u once per launch)."""
     z = _sizes(w)
     per = 2 * z["P"] + 2 * w.dk * z["es"] + w.dv * z["es"] + z["lsz"] + w.dv * 4
-    per += 4 if z["delta"] else 4 * w.dk
-    return per * w.BH
+    per += 4 if z["delta"] else 0
+    return per * w.BH + z["u"]
 
 
 def modelled_step_bytes(w) -> float:
     """Per-step bytes of the method averaged over an M-cycle (one launch per
     step): P(1 + 1/M) + E((M-1)/M + (M-1)/2) + I per slot-head, E the bytes of
-    one log entry, I the step's inputs and outputs."""
+    one log entry, I the step's inputs and outputs; plus RWKV6's u once."""
     z = _sizes(w)
     M = w.M
     E = w.dk * z["es"] + w.dv * z["bsz"] + z["lsz"]
-    I = 2 * w.dk * z["es"] + w.dv * z["es"] + w.dv * 4 + z["lsz"] + (4 if z["delta"] else 4 * w.dk)
-    return (z["P"] * (1 + 1 / M) + E * ((M - 1) / M + (M - 1) / 2) + I) * w.BH
+    I = 2 * w.dk * z["es"] + w.dv * z["es"] + w.dv * 4 + z["lsz"] + (4 if z["delta"] else 0)
+    return (z["P"] * (1 + 1 / M) + E * ((M - 1) / M + (M - 1) / 2) + I) * w.BH + z["u"]
 
 
 # ------------------------------------------------------------------- setup --
@@ -368,14 +378,14 @@ def run_per_slot(w, inp, R: int, K: int, W: int):
         """Issue `count` launches; with count_bytes(b) -> bool, also sum the
         algorithmic bytes of the slots it selects from the host mirror of
         every slot's log length."""
-        ones = w.with_(B=1, H=w.H)
         tot = 0
         for _ in range(count):
             i = pos[0]
             st = sts[i % R]
             if count_bytes is not None:
-                tot += sum(step_launch_bytes(ones, n, n + 1 == w.M)
-                           for n in (st.slot_log_len(b) for b in range(w.B) if count_bytes(b)))
+                ns = [st.slot_log_len(b) for b in range(w.B) if count_bytes(b)]
+                tot += sum(slot_head_bytes(w, n, n + 1 == w.M) * w.H for n in ns)
+                tot += _sizes(w)["u"] if ns else 0
             q, k, v, beta, ld = ptrs[i % pool]
             if L.dl_decode_step(st._h, q, k, v, beta, ld, o.data_ptr(), sp) != 0:
                 raise RuntimeError("dl_decode_step failed on a per-slot state")
@@ -595,6 +605,13 @@ def deep_rotation(w, K: int, W: int, R: int, pool: int) -> dict:
                 deltalog_speedup=round(ems / ms, 3))
 
 
+def pattern_cycle_writes(count: int, R: int, M: int) -> list:
+    """Write flag of each pass of the pattern ceiling's merge cycles: pass i
+    goes to state i % R, as launch i of launch_order does, and rewrites on the
+    M-th pass of each state's cycle, where the step would merge."""
+    return [int((i // R) % M == M - 1) for i in range(count)]
+
+
 def pattern_ceiling(w, R: int, ms_step: float) -> dict | None:
     """The HBM rate that the step kernel's own access pattern on the state
     reaches on this GPU, as context for the roofline (whose peak stays the
@@ -632,10 +649,10 @@ def pattern_ceiling(w, R: int, ms_step: float) -> dict | None:
     M = w.M
 
     def passes(kind, count):
-        # kind 0: reads, 1: rewrites, 2: merge cycles (launch i: state i % R,
-        # the M-th pass of each state's cycle a rewrite)
+        # kind 0: reads, 1: rewrites, 2: merge cycles (pattern_cycle_writes)
+        writes = pattern_cycle_writes(count, R, M) if kind == 2 else [kind] * count
         for i in range(count):
-            write = kind if kind < 2 else int((i // R) % M == M - 1)
+            write = writes[i]
             if lib.dlc_tile_pass(states[i % R].data_ptr(), w.BH, w.dk, w.dv, write, sink.data_ptr(),
                                  float("nan"), sp) != 0:
                 raise RuntimeError("dlc_tile_pass failed")
