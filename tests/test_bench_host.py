@@ -2,7 +2,7 @@
 cycles at any --steps, and the byte model gives the traffic model's figures
 for the three serving workloads (P(1 + 1/M) + E((M-1)/M + (M-1)/2) + I per
 slot-head and step, the "Traffic model" section of the gist.science
-technical summary, priced with this build's log layout: a_t in the input
+technical summary, priced with the library's log layout: a_t in the input
 dtype, b_t in fp32 (RWKV6: the input dtype), the log-decay in fp32)."""
 import pytest
 
