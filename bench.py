@@ -18,7 +18,9 @@ launches are issued directly on one stream, the host running ahead of the
 GPU.  Beside them: the same rounds replayed from HIP graphs (one graph per
 window of the staged input pool; each replay starts with a gap of about 9 us
 on this ROCm, about 0.28 us per launch), and the same direct launches timed
-before the process replayed any graph (about 3% slower, a HIP runtime effect).
+before the process replayed any graph (about 3% slower: direct launches on
+one stream run slower until a kernel has run on a second stream, which a
+graph replay does; an effect below the library).
 The default workload is GDN B=64 H=32 d_k=d_v=128 M=8 with bf16 q/k/v and an
 fp32 state.
 
@@ -507,10 +509,11 @@ def bench_workload(w, K, W, R, pool, with_eager=True, with_staged=True, quick=Fa
     prewarm(launch, R, M, pool)
     # Order of the legs: direct launches in a process that has replayed no HIP
     # graph yet (if none ran before this call), then the graph-replayed leg,
-    # then the direct headline.  Direct launches were measured 3% slower until
-    # the process first replays a HIP graph (any graph, even one of a single
-    # unrelated torch op; from the second timed region after it they settle),
-    # an effect of the HIP runtime whose cause is not identified here.
+    # then the direct headline.  Direct launches on one stream were measured
+    # 3% slower until a kernel has run on a second stream (a graph replay
+    # does that, as does one torch op on a new stream; from the second timed
+    # region after it they settle), an effect below the library whose cause
+    # is not identified here.
     fresh = time_cycles(launch, R, M, pool, K, W, graphs=False)
     gms = time_cycles(launch, R, M, pool, K, W, graphs=True)
     ms = time_cycles(launch, R, M, pool, K, W, graphs=False)
